@@ -1,0 +1,213 @@
+"""Throughput of the fused attention + Ulysses slab re-layout on one MI355X.
+
+One step = one launch of the fused kernel over the whole workload (every
+output tile: Q-loop over K/V tiles, online softmax, PV, slab-store epilogue),
+inputs already resident in HBM.  Default workload: the Video-DiT share
+(B=1, H=5, S=32760 tokens of a 21x30x52 latent, D=128, P=8 slabs, per-head K
+scale U(0.5, 2)), the long-sequence case the throughput target is stated for.
+
+Prints one JSON line on stdout.  Besides the headline TFLOP/s it reports:
+  * roofline: the fused kernel's algorithmic FLOP per launch over its mean
+    launch time (HIP events on the launch stream) against the bf16 dense MFMA
+    peak; `traffic` comes from the committed rocprofv3 counter summary when it
+    was taken on the current kernel source, else null;
+  * fused_store_overhead_pct: median fused / median plain-output time - 1,
+    from alternating launches of the same kernel writing [B][H][S][D];
+  * cpu_baseline: the float64 CPU oracle timed on a bounded sample of the
+    same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["flashattention_output_re_amd/csrc/fa_fwd_kernel.hip",
+                  "flashattention_output_re_amd/csrc/fa_fwd_kernel.h"]
+WORKLOAD_KEYS = {"video": "video-dit-share", "long": "long-video-share",
+                 "image": "image-dit-share", "sparse": "block-sparse-video", "tiny": "tiny"}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_slab_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(name: str, target_s: float):
+    """Time the float64 oracle on a fixed sample of 128-query row blocks."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    w = wl.WORKLOADS[name]
+    inp = wl.make(name)
+    q, k, v = inp.f64("q")[:, :1], inp.f64("k")[:, :1], inp.f64("v")[:, :1]
+    mask = None if inp.mask is None else inp.mask[:1]
+    blocks = 0
+    t0 = time.perf_counter()
+    while True:
+        rows = np.arange(128 * blocks, min(w.S, 128 * blocks + 128))
+        oracle.attention(q, k, v, w.scale, mask, rows=rows)
+        blocks += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or 128 * blocks >= w.S:
+            break
+    n_rows = min(w.S, 128 * blocks)
+    flop = 4.0 * w.B * n_rows * w.S * w.D      # oracle scores every key (masked ones too)
+    return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{name}: head 0, query rows 0..{n_rows - 1} ({blocks} blocks of 128) "
+                      f"against all {w.S} keys, float64 numpy, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video", choices=sorted(WORKLOAD_KEYS))
+    ap.add_argument("--overhead-pairs", type=int, default=30)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU leg "
+              "(the head-to-sequence exchange is stored into local slabs); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import flashattention_output_re_amd as fa
+    import workloads as wl
+
+    fa.load_library()
+    w = wl.WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    inp = wl.make(a.workload)
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    mask = None
+    keep = None
+    if inp.mask is not None:
+        mask = torch.from_numpy(inp.mask.view(np.int64)).to(dev)
+        keep = wl.tile_mask_bool(w.H, w.S, w.keep_prob, w.seed)
+    flop = wl.flop_count(w.B, w.H, w.S, w.D, keep)
+    slabs = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device=dev)
+    plain = torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        fa.attn_fwd_relayout_async(q, k, v, slabs, w.B, w.H, w.S, w.D, w.P, w.scale, mask, stream)
+
+    def plain_out():
+        fa.attn_fwd_plain_async(q, k, v, plain, w.B, w.H, w.S, w.D, w.scale, mask, stream)
+
+    for _ in range(a.warmup):
+        fused()
+        plain_out()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K fused steps, per-launch HIP events.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(a.steps):
+        fused()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)]
+    ms_step = wall * 1e3 / a.steps
+    mean_launch_ms = float(np.mean(launch_ms))
+    tflops = flop / (ms_step * 1e-3) / 1e12
+
+    # ---- fused-store overhead: alternating fused / plain launches.
+    fus, pla = [], []
+    for i in range(a.overhead_pairs):
+        order = (fused, plain_out) if i % 2 == 0 else (plain_out, fused)
+        for fn in order:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            (fus if fn is fused else pla).append(e0.elapsed_time(e1))
+    med_f, med_p = float(np.median(fus)), float(np.median(pla))
+    overhead = (med_f / med_p - 1.0) * 100.0
+    rng = np.random.default_rng(0)
+    boot = []
+    fa_, pa_ = np.array(fus), np.array(pla)
+    for _ in range(2000):
+        boot.append(np.median(rng.choice(fa_, fa_.size)) / np.median(rng.choice(pa_, pa_.size)))
+    ci = [float((np.percentile(boot, 2.5) - 1) * 100), float((np.percentile(boot, 97.5) - 1) * 100)]
+
+    achieved = flop / (mean_launch_ms * 1e-3) / 1e12
+    traffic = load_traffic(a.workload)
+    out = {
+        "metric": "fused attn+relayout TFLOP/s at 1 GPU; % bf16 MFMA peak; fused-store overhead %",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_KEYS[a.workload], "B": w.B, "H": w.H, "S": w.S,
+                   "D": w.D, "P": w.P, "scale": w.scale, "seed": w.seed,
+                   "mask_density": None if keep is None else float(keep.mean()),
+                   "algorithmic_flop": flop},
+        "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
+        "fused_store_overhead_pct": round(overhead, 2),
+        "fused_store_overhead_ci95": [round(c, 2) for c in ci],
+        "median_ms": {"fused": round(med_f, 4), "plain": round(med_p, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "fa_fwd_kernel<128, Slab>",
+                     "mean_launch_ms": round(mean_launch_ms, 4)},
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+// C ABI of libfa_relayout.so: argument validation (pure host code, run before
+// any HIP call), per-device launch geometry, and the exported entry points
+// declared in include/fa_relayout.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/fa_relayout.h"
+#include "fa_fwd_kernel.h"
+
+namespace {
+
+constexpr int kQTile = 128;
+constexpr int kMaxDevices = 64;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shared checks of both layouts.  P == 1 for the plain layout.
+int validate(const void* q, const void* k, const void* v, const void* out, int B, int H, int S,
+             int D, int P, float scale, const uint64_t* mask) {
+  if (!q || !k || !v || !out) return FA_EINVAL;
+  if (B <= 0 || H <= 0 || S <= 0 || P <= 0) return FA_EINVAL;
+  if (!std::isfinite(scale)) return FA_EINVAL;
+  if (D != 64 && D != 128) return FA_EUNSUPPORTED;
+  if (S % P != 0) return FA_EDIV;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return FA_EALIGN;
+  if (mask && !aligned(mask, 8)) return FA_EALIGN;
+  // Per-head slices are addressed with 32-bit byte offsets.
+  if ((int64_t)S * D * 2 > (int64_t)INT32_MAX) return FA_ERANGE;
+  const int64_t nqt = (S + kQTile - 1) / kQTile;
+  if ((int64_t)B * H * nqt > (int64_t)INT32_MAX) return FA_ERANGE;
+  if ((int64_t)H * nqt * ((nqt + 63) / 64) > ((int64_t)1 << 40)) return FA_ERANGE;
+  return FA_OK;
+}
+
+struct DeviceGeom {
+  int cus = 0;
+  int occ[2][2] = {{0, 0}, {0, 0}};   // [D == 128][mode]
+};
+
+std::mutex g_geom_mutex;
+DeviceGeom g_geom[kMaxDevices];
+
+// Persistent grid size for (D, mode) on the current device: every resident
+// workgroup slot of the chip, or -1 if the device cannot be queried.
+int grid_cap_for(int D, fa::StoreMode mode) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  std::lock_guard<std::mutex> lock(g_geom_mutex);
+  DeviceGeom& gm = g_geom[dev];
+  if (gm.cus == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return -1;
+    gm.cus = cus;
+  }
+  int& occ = gm.occ[D == 128][(int)mode];
+  if (occ == 0) {
+    int blocks = 0;
+    if (fa::kernel_occupancy(D, mode, &blocks) != 0 || blocks <= 0) return -1;
+    occ = blocks;
+  }
+  return gm.cus * occ;
+}
+
+int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* out, int B, int H,
+        int S, int D, int P, float scale, const uint64_t* mask, hipStream_t stream) {
+  const int st = validate(q, k, v, out, B, H, S, D, P, scale, mask);
+  if (st != FA_OK) return st;
+  const int cap = grid_cap_for(D, mode);
+  if (cap <= 0) return FA_EDEVICE;
+  fa::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = static_cast<uint16_t*>(out);
+  p.mask = mask;
+  p.B = B;
+  p.H = H;
+  p.S = S;
+  p.P = P;
+  p.Sp = S / P;
+  p.nqt = (S + kQTile - 1) / kQTile;
+  p.units = B * H * p.nqt;
+  p.nmt = p.nqt;
+  p.mw = (p.nmt + 63) / 64;
+  p.c = (float)((double)scale * 1.4426950408889634073599246810019);
+  return fa::launch_fwd(D, mode, p, cap, stream) == 0 ? FA_OK : FA_ELAUNCH;
+}
+
+int finish_blocking(int st) {
+  if (st != FA_OK) return st;
+  return hipStreamSynchronize(nullptr) == hipSuccess ? FA_OK : FA_EEXEC;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_relayout_async(const void* q, const void* k, const void* v, void* out_slabs, int B,
+                            int H, int S, int D, int P, float scale, const uint64_t* mask,
+                            void* stream) {
+  return run(fa::StoreMode::Slab, q, k, v, out_slabs, B, H, S, D, P, scale, mask,
+             static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_relayout(const void* q, const void* k, const void* v, void* out_slabs, int B, int H,
+                      int S, int D, int P, float scale, const uint64_t* mask) {
+  return finish_blocking(
+      run(fa::StoreMode::Slab, q, k, v, out_slabs, B, H, S, D, P, scale, mask, nullptr));
+}
+
+int attn_fwd_plain_async(const void* q, const void* k, const void* v, void* out, int B, int H,
+                         int S, int D, float scale, const uint64_t* mask, void* stream) {
+  return run(fa::StoreMode::Plain, q, k, v, out, B, H, S, D, 1, scale, mask,
+             static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_plain(const void* q, const void* k, const void* v, void* out, int B, int H, int S,
+                   int D, float scale, const uint64_t* mask) {
+  return finish_blocking(
+      run(fa::StoreMode::Plain, q, k, v, out, B, H, S, D, 1, scale, mask, nullptr));
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_EINVAL: return "invalid argument (null tensor, non-positive size or non-finite scale)";
+    case FA_EDIV: return "S is not a multiple of the slab count P";
+    case FA_EUNSUPPORTED: return "unsupported head dimension (D must be 64 or 128)";
+    case FA_EALIGN: return "misaligned pointer (tensors need 16 bytes, the mask 8)";
+    case FA_ERANGE: return "sizes exceed the kernel's index range";
+    case FA_ELAUNCH: return "kernel launch failed";
+    case FA_EDEVICE: return "no usable HIP device";
+    case FA_EEXEC: return "kernel execution failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_abi_version(void) { return FA_ABI_VERSION; }
+
+}  // extern "C"

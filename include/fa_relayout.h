@@ -1,0 +1,103 @@
+/*
+ * fa_relayout.h -- fused FlashAttention forward + Ulysses head-to-sequence
+ * re-layout for MI355X (gfx950).  C ABI of libfa_relayout.so.
+ *
+ * What it computes.  One GPU's share of Ulysses sequence-parallel attention
+ * in diffusion-transformer inference (X-Stage abstract, CatalyzeX and fugumt
+ * pages): for its H local heads over the whole sequence of S tokens, each
+ * 128-query output tile runs a non-causal FlashAttention forward pass (online
+ * softmax over K/V tiles), and its owner stores the finished tile straight
+ * into the sequence-sharded layout before resuming the next tile's Q-loop,
+ * with no separate communication wavefront ("Technical Summary: X-Stage in
+ * DiT Inference", Key Contributions 3, FlashAttention-A2A piggybacking).  On
+ * one GPU the P destinations of the post-attention All-to-All are P local
+ * slabs.  An optional per-head bitmask skips 128x128 tiles (bit-wise
+ * block-sparse attention, ScalingAttention abstract on the CatalyzeX page).
+ *
+ *   O[b][h][s] = sum_j softmax_j(scale * <Q[b][h][s], K[b][h][j]>) V[b][h][j]
+ *   slab p = s / (S/P), t = s % (S/P):
+ *   out_slabs[p][b][t][h][d] = O[b][h][s][d]       (rounded to bf16, RNE)
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing, keeps no pointer after return and holds no
+ *     state between calls other than a per-device cache of the CU count and
+ *     occupancy; calls on different streams may run concurrently.
+ *   - q, k, v: bf16 [B][H][S][D], contiguous, 16-byte aligned.
+ *   - scale: multiplies Q K^T before the softmax; any finite value (0 gives
+ *     the mean of V; negative values are allowed).
+ *   - mask: NULL for dense attention, else a device array of uint64 words
+ *     [H][nT][W] with nT = ceil(S/128), W = ceil(nT/64), 8-byte aligned.
+ *     Tile (i, j) of head h -- queries [128 i, 128 i + 128) against keys
+ *     [128 j, 128 j + 128) -- takes part iff bit (j % 64) of word j / 64 of
+ *     row (h, i) is set.  The same mask applies to every batch index.
+ *     Masked tiles contribute nothing to the softmax; a query row whose
+ *     tiles are all masked gets an output row of zeros.
+ *   - Keys at positions >= S do not exist (the ragged last tile is handled);
+ *     rows >= S are never written.
+ *   - Validation happens before any HIP call: on an error nothing is
+ *     launched and nothing is written.
+ *   - The _async entry points enqueue on `stream` (a hipStream_t; NULL is the
+ *     null stream) and return; faults inside the kernel surface at the
+ *     caller's next synchronisation.  The entry points without _async enqueue
+ *     on the null stream and wait for completion, so they also report
+ *     execution errors.
+ *   - Outputs must not overlap the inputs (undefined behaviour otherwise).
+ *
+ * Return value: FA_OK (0) or one of the negative status codes below.
+ */
+#ifndef FA_RELAYOUT_H
+#define FA_RELAYOUT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_OK 0
+#define FA_EINVAL (-1)        /* null q/k/v/out; B, H, S or P <= 0; scale not finite */
+#define FA_EDIV (-2)          /* S is not a multiple of P */
+#define FA_EUNSUPPORTED (-3)  /* D is not 64 or 128 */
+#define FA_EALIGN (-4)        /* a tensor pointer not 16-byte aligned, mask not 8 */
+#define FA_ERANGE (-5)        /* S*D*2 bytes per head >= 2^31, or too many tiles */
+#define FA_ELAUNCH (-6)       /* the kernel launch was rejected */
+#define FA_EDEVICE (-7)       /* no usable HIP device, or device query failed */
+#define FA_EEXEC (-8)         /* (blocking entry points) execution failed */
+
+#define FA_ABI_VERSION 1
+
+/* Fused attention + slab store (the hot path).
+ * out_slabs: bf16 [P][B][S/P][H][D], contiguous, 16-byte aligned; slab p is
+ * the P-th contiguous block of B*(S/P)*H*D elements.  Enqueues on `stream`. */
+int attn_fwd_relayout_async(const void* q, const void* k, const void* v,
+                            void* out_slabs, int B, int H, int S, int D, int P,
+                            float scale, const uint64_t* mask, void* stream);
+
+/* As attn_fwd_relayout_async on the null stream, then waits for completion. */
+int attn_fwd_relayout(const void* q, const void* k, const void* v,
+                      void* out_slabs, int B, int H, int S, int D, int P,
+                      float scale, const uint64_t* mask);
+
+/* The same attention kernel writing the plain layout out[b][h][s][d]
+ * (bf16 [B][H][S][D]) instead of the slabs: the measurement twin that the
+ * fused store's overhead is taken against ("FlashAttention alone").  Same
+ * arithmetic, so its values equal the slab output bit for bit. */
+int attn_fwd_plain_async(const void* q, const void* k, const void* v, void* out,
+                         int B, int H, int S, int D, float scale,
+                         const uint64_t* mask, void* stream);
+
+int attn_fwd_plain(const void* q, const void* k, const void* v, void* out,
+                   int B, int H, int S, int D, float scale, const uint64_t* mask);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* attn_status_string(int status);
+
+/* FA_ABI_VERSION of the loaded library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_RELAYOUT_H */

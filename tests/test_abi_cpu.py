@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments before touching HIP (CPU only, no compute calls)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+from flashattention_output_re_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_relayout.h")
+
+# Fake, 16-byte aligned device addresses.  Only ever passed in calls that fail
+# validation, which returns before any HIP call.
+A, B_, C, O, M = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
+
+
+def declared_status_codes():
+    return {name: int(val) for name, val in
+            re.findall(r"#define\s+(FA_E\w+|FA_OK)\s+\(?(-?\d+)\)?", _header())}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_matches_header(lib):
+    v = int(re.search(r"#define\s+FA_ABI_VERSION\s+(\d+)", _header()).group(1))
+    assert lib.attn_abi_version() == v == binding.attn_abi_version()
+
+
+def test_status_codes_and_strings(lib):
+    codes = declared_status_codes()
+    assert {v: k for k, v in codes.items()} == binding.STATUS_NAMES
+    seen = set()
+    for code in codes.values():
+        s = binding.attn_status_string(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == len(codes)
+    assert binding.attn_status_string(12345) == "unknown status"
+
+
+def _relayout(lib, q=A, k=B_, v=C, out=O, Bn=1, H=2, S=256, D=128, P=2, scale=0.1, mask=None):
+    return lib.attn_fwd_relayout_async(q, k, v, out, Bn, H, S, D, P, scale, mask, None)
+
+
+def _plain(lib, q=A, k=B_, v=C, out=O, Bn=1, H=2, S=256, D=128, scale=0.1, mask=None):
+    return lib.attn_fwd_plain_async(q, k, v, out, Bn, H, S, D, scale, mask, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(out=None), -1),
+    (dict(Bn=0), -1), (dict(H=0), -1), (dict(S=0), -1), (dict(P=0), -1), (dict(S=-5), -1),
+    (dict(scale=math.inf), -1), (dict(scale=math.nan), -1), (dict(scale=-math.inf), -1),
+    (dict(S=255, P=2), -2), (dict(S=32760, P=16), -2),
+    (dict(D=32), -3), (dict(D=96), -3), (dict(D=256), -3), (dict(D=0), -3),
+    (dict(q=A + 8), -4), (dict(k=B_ + 2), -4), (dict(v=C + 4), -4), (dict(out=O + 8), -4),
+    (dict(mask=M + 4), -4),
+    (dict(S=(1 << 23), D=128, P=1), -5),
+    (dict(Bn=1 << 15, H=1 << 15, S=256, P=1), -5),
+])
+def test_relayout_validation(lib, kw, code):
+    assert _relayout(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(H=-1), -1), (dict(scale=math.nan), -1),
+    (dict(D=100), -3), (dict(out=O + 2), -4), (dict(S=(1 << 23)), -5),
+])
+def test_plain_validation(lib, kw, code):
+    assert _plain(lib, **kw) == code
+
+
+def test_blocking_entry_points_validate(lib):
+    assert lib.attn_fwd_relayout(None, B_, C, O, 1, 1, 256, 128, 2, 0.1, None) == -1
+    assert lib.attn_fwd_relayout(A, B_, C, O, 1, 1, 256, 128, 3, 0.1, None) == -2
+    assert lib.attn_fwd_plain(A, B_, C, O, 1, 1, 256, 48, 0.1, None) == -3
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
+def test_valid_arguments_without_device_report_no_device(lib):
+    assert _relayout(lib) == -7
+    assert _plain(lib) == -7
+
+
+def test_python_binding_raises(lib):
+    with pytest.raises(binding.FaError) as e:
+        lib_call = binding.attn_fwd_relayout_async
+        lib_call(None, None, None, None, 1, 1, 256, 64, 3, 0.125, stream=0)
+    assert e.value.name == "FA_EINVAL"
+
+
+def test_binding_rejects_wrong_tensors():
+    t = torch.zeros((1, 1, 256, 64), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        binding._check_tensor("q", t, (1, 1, 256, 64))
+    tb = t.to(torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding._check_tensor("q", tb, (1, 1, 256, 64))   # not on a device

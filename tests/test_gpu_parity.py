@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Gate (attention values, bf16 outputs vs the unrounded float64 reference):
+max-abs <= 1e-2 and mean-abs <= 1e-3 over every compared element.  The
+re-layout is checked bit-exactly with integer-tagged inputs, with canary-filled
+output buffers inside guard bands (every slab element written, nothing
+outside).  Full-size workloads are compared on sampled rows (tile edges, slab
+edges, the ragged tail, random rows) that the oracle computes row by row.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import (assert_close, assert_within_bound, f64, mask_to_dev, run_plain, run_slabs, sample_rows,
+                      slab_rows, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _upload(inp):
+    return to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), mask_to_dev(inp.mask)
+
+
+# ------------------------------------------------------------ full oracle
+@pytest.mark.parametrize("name", ["tiny", "image"])
+def test_workload_full_parity(name):
+    w = wl.WORKLOADS[name]
+    say(f"[parity] {name} B={w.B} H={w.H} S={w.S} D={w.D} P={w.P}")
+    inp = wl.make(name)
+    q, k, v, m = _upload(inp)
+    slabs = run_slabs(q, k, v, w.P, w.scale, m)
+    plain = run_plain(q, k, v, w.scale, m)
+    ref = oracle.attention(inp.f64("q"), inp.f64("k"), inp.f64("v"), w.scale, inp.mask)
+    e = assert_close(f64(slabs), oracle.relayout_index(ref, w.P), name)
+    assert_close(f64(plain), ref, name + " plain")
+    absv = oracle.attention(inp.f64("q"), inp.f64("k"), np.abs(inp.f64("v")), w.scale, inp.mask)
+    assert_within_bound(f64(plain), ref, absv, name)
+    # Same arithmetic, two store layouts: identical bits.
+    assert torch.equal(slabs.view(torch.int16).cpu(),
+                       torch.from_numpy(oracle.relayout_split(
+                           plain.view(torch.int16).cpu().numpy(), w.P)))
+    say(f"[parity] {name}: {e}")
+
+
+@pytest.mark.parametrize("name", ["video", "long", "sparse"])
+def test_workload_sampled_parity(name):
+    w = wl.WORKLOADS[name]
+    say(f"[parity] {name} sampled rows B={w.B} H={w.H} S={w.S} D={w.D} P={w.P}")
+    inp = wl.make(name)
+    q, k, v, m = _upload(inp)
+    slabs = run_slabs(q, k, v, w.P, w.scale, m)
+    rows = sample_rows(w.S, w.P, seed=w.seed)
+    ref = oracle.attention(inp.f64("q"), inp.f64("k"), inp.f64("v"), w.scale, inp.mask,
+                           rows=rows)
+    got = slab_rows(slabs, rows, w.S, w.P)
+    e = assert_close(got, ref, name)
+    absv = oracle.attention(inp.f64("q"), inp.f64("k"), np.abs(inp.f64("v")), w.scale, inp.mask,
+                            rows=rows)
+    assert_within_bound(got, ref, absv, name)
+    say(f"[parity] {name}: {len(rows)} rows x {w.H} heads: {e}")
+    # The plain twin equals the slabs bit for bit at full size.
+    plain = run_plain(q, k, v, w.scale, m)
+    re = torch.from_numpy(oracle.relayout_split(plain.view(torch.int16).cpu().numpy(), w.P))
+    assert torch.equal(slabs.view(torch.int16).cpu(), re)
+
+
+# ------------------------------------------------------ bit-exact re-layout
+@pytest.mark.parametrize("name", ["tiny", "image", "video", "long", "sparse"])
+def test_tags_bit_exact(name):
+    w = wl.WORKLOADS[name]
+    say(f"[tags] {name} S={w.S} H={w.H} D={w.D} P={w.P}")
+    t = wl.tag_inputs(w.B, w.H, w.S, w.D)
+    mask = None
+    if w.keep_prob is not None:
+        mask = wl.pack_mask(wl.tile_mask_bool(w.H, w.S, w.keep_prob, w.seed))
+    q, k, v = to_dev(t.q), to_dev(t.k), to_dev(t.v)
+    slabs = run_slabs(q, k, v, w.P, w.scale, mask_to_dev(mask))
+    want = oracle.relayout_index(t.v.view(torch.int16).numpy(), w.P)
+    got = slabs.view(torch.int16).cpu().numpy()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("B,H,S,D,P", [
+    (2, 3, 256, 64, 2), (2, 2, 1000, 128, 8), (1, 4, 4095 * 2, 128, 2), (3, 1, 384, 128, 3),
+    (1, 2, 129, 64, 1), (1, 1, 1, 128, 1), (2, 2, 17, 64, 17),
+])
+def test_tags_shapes(B, H, S, D, P):
+    t = wl.tag_inputs(B, H, S, D)
+    q, k, v = to_dev(t.q), to_dev(t.k), to_dev(t.v)
+    slabs = run_slabs(q, k, v, P, 1.0 / math.sqrt(D))
+    want = oracle.relayout_index(t.v.view(torch.int16).numpy(), P)
+    assert np.array_equal(slabs.view(torch.int16).cpu().numpy(), want)
+
+
+# ---------------------------------------------------------------- edges
+EDGE_SHAPES = [
+    (1, 1, 1, 64, 1), (1, 1, 2, 128, 2), (1, 2, 16, 64, 4), (1, 1, 63, 128, 1),
+    (1, 1, 64, 128, 1), (1, 1, 65, 64, 5), (1, 2, 127, 128, 1), (1, 1, 128, 64, 8),
+    (1, 2, 129, 128, 3), (2, 2, 200, 64, 8), (2, 1, 255, 128, 5), (1, 3, 257, 128, 1),
+    (2, 3, 640, 128, 8), (1, 2, 1000, 64, 8),
+]
+
+
+@pytest.mark.parametrize("B,H,S,D,P", EDGE_SHAPES)
+def test_edge_shapes(B, H, S, D, P):
+    q, k, v = wl.random_qkv(B, H, S, D, seed=S * 7 + D)
+    scale = 1.0 / math.sqrt(D)
+    slabs = run_slabs(to_dev(q), to_dev(k), to_dev(v), P, scale)
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    ref = oracle.attention(qd, kd, vd, scale)
+    absv = oracle.attention(qd, kd, np.abs(vd), scale)
+    assert_within_bound(f64(slabs), oracle.relayout_split(ref, P), oracle.relayout_split(absv, P),
+                        f"{(B, H, S, D, P)}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, -1.0 / math.sqrt(128)])
+def test_scales(scale):
+    B, H, S, D, P = 1, 2, 300, 128, 3
+    q, k, v = wl.random_qkv(B, H, S, D, seed=11)
+    slabs = run_slabs(to_dev(q), to_dev(k), to_dev(v), P, scale)
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    ref = oracle.attention(qd, kd, vd, scale)
+    absv = oracle.attention(qd, kd, np.abs(vd), scale)
+    assert_within_bound(f64(slabs), oracle.relayout_split(ref, P), oracle.relayout_split(absv, P),
+                        f"scale={scale}")
+
+
+def test_scale_zero_is_mean_of_v():
+    B, H, S, D, P = 1, 2, 333, 64, 3
+    q, k, v = wl.random_qkv(B, H, S, D, seed=12)
+    slabs = run_slabs(to_dev(q), to_dev(k), to_dev(v), P, 0.0)
+    mean = v.double().numpy().mean(axis=2, keepdims=True)
+    assert_close(f64(slabs), oracle.relayout_split(np.broadcast_to(mean, (B, H, S, D)), P))
+
+
+def test_ones_v_gives_ones():
+    B, H, S, D = 1, 3, 4096, 128
+    q, k, _ = wl.random_qkv(B, H, S, D, seed=13, kscale=(0.5, 2.0))
+    v = torch.ones((B, H, S, D), dtype=torch.bfloat16)
+    out = f64(run_plain(to_dev(q), to_dev(k), to_dev(v), 1.0 / math.sqrt(D)))
+    assert np.abs(out - 1.0).max() <= 2 ** -7
+
+
+# ---------------------------------------------------------------- masks
+def test_full_mask_equals_dense():
+    B, H, S, D, P = 1, 3, 1000, 128, 8
+    q, k, v = (to_dev(t) for t in wl.random_qkv(B, H, S, D, seed=14))
+    keep = np.ones((H, 8, 8), dtype=bool)
+    a = run_slabs(q, k, v, P, 0.09, mask_to_dev(wl.pack_mask(keep)))
+    b = run_slabs(q, k, v, P, 0.09)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("S,p_keep", [(1000, 0.0), (1000, 0.3), (32760 // 4, 0.3), (700, 0.7)])
+def test_masked_parity(S, p_keep):
+    B, H, D, P = 1, 3, 128, 4 if S % 4 == 0 else 1
+    q, k, v = wl.random_qkv(B, H, S, D, seed=S + 1)
+    keep = wl.tile_mask_bool(H, S, p_keep, seed=S)
+    words = wl.pack_mask(keep)
+    slabs = run_slabs(to_dev(q), to_dev(k), to_dev(v), P, 0.088, mask_to_dev(words))
+    rows = None if S <= 1000 else sample_rows(S, P, seed=S)
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    ref = oracle.attention(qd, kd, vd, 0.088, words, rows=rows)
+    absv = oracle.attention(qd, kd, np.abs(vd), 0.088, words, rows=rows)
+    if rows is None:
+        got, ref, absv = f64(slabs), oracle.relayout_split(ref, P), oracle.relayout_split(absv, P)
+    else:
+        got = slab_rows(slabs, rows, S, P)
+    assert_close(got, ref, f"mask S={S}")
+    assert_within_bound(got, ref, absv, f"mask S={S}")
+
+
+def test_identical_keys_with_mask_is_mean_over_kept():
+    B, H, S, D, P = 1, 2, 500, 64, 4
+    q, _, v = wl.random_qkv(B, H, S, D, seed=15)
+    k = q[:, :, :1].expand(B, H, S, D).contiguous()
+    keep = wl.tile_mask_bool(H, S, 0.5, seed=15)
+    out = f64(run_plain(to_dev(q), to_dev(k), to_dev(v), 0.125, mask_to_dev(wl.pack_mask(keep))))
+    vv = v.double().numpy()
+    tile = np.arange(S) // 128
+    for h in range(H):
+        for i in range(keep.shape[1]):
+            cols = keep[h, i][tile]
+            want = vv[0, h][cols].mean(axis=0)
+            got = out[0, h][tile == i]
+            assert np.abs(got - want).max() <= 1e-2
+
+
+def test_fully_masked_rows_are_zero():
+    B, H, S, D = 1, 1, 384, 128
+    q, k, v = wl.random_qkv(B, H, S, D, seed=16)
+    keep = np.zeros((1, 3, 3), dtype=bool)
+    keep[0, 0, 0] = keep[0, 2, 1] = True      # tile row 1 keeps nothing
+    words = wl.pack_mask(keep)
+    out = f64(run_plain(to_dev(q), to_dev(k), to_dev(v), 0.1, mask_to_dev(words)))
+    assert np.all(out[0, 0, 128:256] == 0.0)
+    ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0.1, words)
+    assert_close(out, ref)
+
+
+# ------------------------------------------------------------ invariants
+def test_key_shift_and_permutation_invariance():
+    B, H, S, D = 1, 2, 1000, 128
+    r = np.random.default_rng(17)
+    # Quarter-integers: K and K + c are both exact in bf16.
+    q = wl.to_bf16(r.integers(-4, 5, (B, H, S, D)) / 4.0)
+    k = r.integers(-4, 5, (B, H, S, D)) / 4.0
+    v = wl.to_bf16(r.standard_normal((B, H, S, D)))
+    c = r.integers(-3, 4, (1, 1, 1, D)).astype(np.float64)
+    scale = 0.05
+    base = f64(run_plain(to_dev(q), to_dev(wl.to_bf16(k)), to_dev(v), scale))
+    shifted = f64(run_plain(to_dev(q), to_dev(wl.to_bf16(k + c)), to_dev(v), scale))
+    assert np.abs(base - shifted).max() <= 1e-2
+    perm = torch.from_numpy(r.permutation(S))
+    kp = wl.to_bf16(k)[:, :, perm].contiguous()
+    vp = v[:, :, perm].contiguous()
+    permuted = f64(run_plain(to_dev(q), to_dev(kp), to_dev(vp), scale))
+    assert np.abs(base - permuted).max() <= 1e-2
+
+
+def test_deterministic_and_stream():
+    w = wl.WORKLOADS["image"]
+    inp = wl.make("image")
+    q, k, v, m = _upload(inp)
+    a = run_slabs(q, k, v, w.P, w.scale)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_slabs(q, k, v, w.P, w.scale, stream=s)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_blocking_entry_points():
+    import flashattention_output_re_amd as fa
+    B, H, S, D, P = 1, 2, 512, 64, 4
+    q, k, v = (to_dev(t) for t in wl.random_qkv(B, H, S, D, seed=18))
+    a = torch.empty((P, B, S // P, H, D), dtype=torch.bfloat16, device=q.device)
+    fa.attn_fwd_relayout(q, k, v, a, B, H, S, D, P, 0.125)
+    b = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=q.device)
+    fa.attn_fwd_plain(q, k, v, b, B, H, S, D, 0.125)
+    re = oracle.relayout_split(b.view(torch.int16).cpu().numpy(), P)
+    assert np.array_equal(a.view(torch.int16).cpu().numpy(), re)
