@@ -9,11 +9,12 @@ import flashattention_output_re_amd as fa
 
 MAX_ABS = 1e-2    # workload gate: max |gpu - oracle| over every compared element
 MEAN_ABS = 1e-3   # workload gate: mean |gpu - oracle|
-# Element-wise bound from the arithmetic: the kernel rounds each softmax weight
-# fed to the PV product to bf16 (relative error <= 2^-9, so the output moves by
-# at most 2^-9 * sum_j P_j |V_j|) and rounds the output to bf16 (<= 2^-9 |O|);
-# fp32 accumulation, exp2 and the division add far less (the floor and slack).
-BOUND_REL = 2.0 ** -9
+# Element-wise bound from the arithmetic.  bf16 keeps 8 significant bits, so
+# round-to-nearest has relative error <= u = 2^-8.  The kernel rounds each
+# softmax weight fed to the PV product to bf16 (the output moves by at most
+# u * sum_j P_j |V_j|) and rounds the output to bf16 (<= u |O|); fp32
+# accumulation, exp2 and the division add far less (the floor and slack).
+BOUND_REL = 2.0 ** -8
 BOUND_SLACK = 1.1
 BOUND_FLOOR = 1e-5
 CANARY = -1       # 0xFFFF as int16: a bf16 NaN pattern the kernel never writes
@@ -96,7 +97,7 @@ def assert_close(got: np.ndarray, want: np.ndarray, what: str = ""):
 
 
 def assert_within_bound(got: np.ndarray, ref: np.ndarray, ref_absv: np.ndarray, what: str = ""):
-    """|got - ref| <= 1.1 * 2^-9 * (|ref| + sum_j P_j |V_j|) + 1e-5 element-wise;
+    """|got - ref| <= 1.1 * 2^-8 * (|ref| + sum_j P_j |V_j|) + 1e-5 element-wise;
     ``ref_absv`` is the oracle's attention output for |V|."""
     assert got.shape == ref.shape == ref_absv.shape
     assert np.isfinite(got).all(), f"{what}: non-finite output"
