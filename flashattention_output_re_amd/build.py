@@ -18,8 +18,10 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["fa_abi.hip", "fa_fwd_kernel.hip"]
 ARCH = "gfx950"
 
-# hipcc must not emit packed fp32 VALU ops (v_pk_fma_f32 and friends).
-HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# hipcc must not emit packed fp32 VALU ops (v_pk_fma_f32 and friends).  The
+# device code never tests for NaN, so max/min need no NaN canonicalisation.
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Xarch_device", "-fno-honor-nans"]
 
 
 def hipcc() -> str:

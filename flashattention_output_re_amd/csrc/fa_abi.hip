@@ -89,6 +89,10 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   p.nmt = p.nqt;
   p.mw = (p.nmt + 63) / 64;
   p.c = (float)((double)scale * 1.4426950408889634073599246810019);
+  // With c == 0 every score weighs exp2(0) = 1; any positive c small enough
+  // that |s| * c rounds away against 1 gives the same weights bit for bit,
+  // and keeps (-inf) * c = -inf for the keys past S.
+  if (p.c == 0.0f) p.c = 1e-30f;
   return fa::launch_fwd(D, mode, p, cap, stream) == 0 ? FA_OK : FA_ELAUNCH;
 }
 

@@ -1,33 +1,39 @@
 // Fused FlashAttention forward + Ulysses slab store for gfx950 (MI355X).
 //
-// One persistent workgroup of 4 wavefronts owns a 128-query output tile of one
-// (batch, head): it streams the K/V tiles of the whole sequence through LDS,
-// runs QK^T and PV on the bf16 MFMA units with an fp32 online softmax, and in
-// the epilogue stores the finished tile straight into the P destination slabs
-// of the head-to-sequence re-layout, then moves on to its next output tile
-// without waiting for those stores ("Technical Summary: X-Stage in DiT
-// Inference", Key Contributions 3: the output-tile owner issues the stores and
-// resumes the next tile's Q-loop; no dedicated communication wavefront).  The
-// same kernel body with StoreMode::Plain writes [B][H][S][D] instead.
+// One persistent workgroup of 4 wavefronts per CU owns 128-query output tiles
+// of one (batch, head) at a time: it streams the K/V tiles of the whole
+// sequence through LDS, runs QK^T and PV on the bf16 MFMA units with an fp32
+// online softmax, and in the epilogue stores the finished tile straight into
+// the P destination slabs of the head-to-sequence re-layout, then moves on to
+// its next output tile without waiting for those stores ("Technical Summary:
+// X-Stage in DiT Inference", Key Contributions 3: the output-tile owner issues
+// the stores and resumes the next tile's Q-loop; no dedicated communication
+// wavefront).  StoreMode::Plain runs the same body but writes [B][H][S][D].
 //
-// Layout choices (all per wavefront, 32 queries):
+// Layout choices (per wavefront, 32 queries):
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims of K from
-//   LDS, B = 16 dims x 32 queries of Q kept in VGPRs.  The accumulator puts one
+//   LDS, B = 16 dims x 32 queries of Q held in VGPRs.  The accumulator puts one
 //   query per lane (lane % 32) and 16 keys per lane, so a row's max and sum are
-//   lane-local except for one exchange between the two wave halves
+//   lane-local apart from one exchange between the wave halves
 //   (v_permlane32_swap).
 //   O^T = V^T P^T: the S^T accumulator, rounded to bf16, is directly the B
-//   operand (same query per lane, keys as the contraction index).  The A
-//   operand needs V transposed; V is written to LDS as V^T with the keys of
-//   each 16-key group permuted so that one ds_read_b128 yields exactly the 8
-//   keys a lane's half of the wave contributes to the contraction.
+//   operand (same query per lane, keys as the contraction index).  V is
+//   written to LDS as V^T with the keys of each 16-key group permuted so that
+//   one ds_read_b128 yields exactly the 8 keys a half-wave contributes.
 //   The O^T accumulator again holds one query per lane; one permlane32 swap
-//   turns its 4-wide d runs into 8 consecutive d, so the epilogue issues
+//   turns its 4-wide runs of d into 8 consecutive d, so the epilogue issues
 //   128-bit stores.
 //
+// Schedule.  On gfx950 a wavefront overlaps an MFMA with the independent VALU
+// work issued after it, so each K/V stage is software-pipelined inside the
+// wave: the QK^T MFMAs of the next stage are interleaved with the softmax of
+// the current one, and the PV MFMAs of the current stage with the LDS staging
+// of the stages after it.  One wave per SIMD (512 VGPRs) holds both score
+// tiles, the Q fragments, the O accumulator and the staging registers.
+//
 // Softmax runs in the log2 domain (c = scale * log2 e, p = exp2(s c - m)).
-// The running max is only raised when a row's new max exceeds it by more than
-// kTau (2^8 headroom for p); the final division by the row sum makes the
+// The running max is only raised when some row of the wave exceeds it by more
+// than kTau (2^8 headroom for p); the final division by the row sum makes the
 // result independent of which max was used.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,6 +52,7 @@ constexpr int BM = 128;          // queries per output tile (= mask tile)
 constexpr int BN = 64;           // keys per LDS stage
 constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
+
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -98,67 +105,78 @@ __device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) ^ d) & 7; }
 template <int D>
 struct Smem {
   static constexpr int KROW = D + 8;                 // padded K row, elements
-  static constexpr int K_ELEMS = BN * KROW;
-  static constexpr int V_ELEMS = D * BN;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * STAGE * 2;        // double buffered, bf16
+  static constexpr int K_ELEMS = BN * KROW;          // one K stage
+  static constexpr int V_ELEMS = D * BN;             // one V^T stage
+  static constexpr int TOTAL = 2 * K_ELEMS + 2 * V_ELEMS;
 };
 
 template <int D>
-struct Stage {
-  static constexpr int KCH = D / 8;                                  // 16 B chunks per row
-  static constexpr int K_PER_T = BN * KCH / kThreads;                // K chunks per thread
-  static constexpr int V_GROUPS = (BN / 4) * KCH;                    // 4 rows x 16 B groups
-  u32x4 k[K_PER_T];
-  u32x4 v[4];
+struct KStage {
+  static constexpr int KCH = D / 8;                      // 16 B chunks per row
+  static constexpr int PER_T = BN * KCH / kThreads;      // chunks per thread
+  u32x4 r[PER_T];
 };
 
 template <int D>
-__device__ __forceinline__ void stage_load(Stage<D>& st, __amdgpu_buffer_rsrc_t rk,
-                                           __amdgpu_buffer_rsrc_t rv, int key0, int tid) {
-  constexpr int KCH = Stage<D>::KCH;
+struct VStage {
+  static constexpr int KCH = D / 8;
+  static constexpr int GROUPS = (BN / 4) * KCH;          // 4 keys x 8 dims per group
+  u32x4 r[4];
+};
+
+template <int D>
+__device__ __forceinline__ void k_load(KStage<D>& st, __amdgpu_buffer_rsrc_t rk, int key0, int tid) {
+  constexpr int KCH = KStage<D>::KCH;
 #pragma unroll
-  for (int i = 0; i < Stage<D>::K_PER_T; ++i) {
+  for (int i = 0; i < KStage<D>::PER_T; ++i) {
     const int idx = tid + kThreads * i;
     const int row = idx / KCH, ch = idx % KCH;
-    st.k[i] = load16(rk, (uint32_t)((key0 + row) * D * 2 + ch * 16));
-  }
-  if (Stage<D>::V_GROUPS >= kThreads || tid < Stage<D>::V_GROUPS) {
-    const int ch = tid % KCH, quad = tid / KCH;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      st.v[r] = load16(rv, (uint32_t)((key0 + 4 * quad + r) * D * 2 + ch * 16));
+    st.r[i] = load16(rk, (uint32_t)((key0 + row) * D * 2 + ch * 16));
   }
 }
 
 template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D>& st, uint16_t* ks, uint16_t* vt,
-                                            int tid) {
-  constexpr int KCH = Stage<D>::KCH;
-  constexpr int KROW = Smem<D>::KROW;
+__device__ __forceinline__ void k_store(const KStage<D>& st, uint16_t* ks, int tid) {
+  constexpr int KCH = KStage<D>::KCH;
 #pragma unroll
-  for (int i = 0; i < Stage<D>::K_PER_T; ++i) {
+  for (int i = 0; i < KStage<D>::PER_T; ++i) {
     const int idx = tid + kThreads * i;
     const int row = idx / KCH, ch = idx % KCH;
-    *reinterpret_cast<u32x4*>(ks + row * KROW + ch * 8) = st.k[i];
+    *reinterpret_cast<u32x4*>(ks + row * Smem<D>::KROW + ch * 8) = st.r[i];
   }
-  if (Stage<D>::V_GROUPS >= kThreads || tid < Stage<D>::V_GROUPS) {
+}
+
+template <int D>
+__device__ __forceinline__ void v_load(VStage<D>& st, __amdgpu_buffer_rsrc_t rv, int key0, int tid) {
+  constexpr int KCH = VStage<D>::KCH;
+  if (VStage<D>::GROUPS >= kThreads || tid < VStage<D>::GROUPS) {
     const int ch = tid % KCH, quad = tid / KCH;
-    const int pos = 16 * (quad >> 2) + 4 * vt_pos_of_quad(quad & 3);   // key position of row 4*quad
-    const int chunk = pos >> 3, half = pos & 7;                        // 16 B chunk, element offset
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      st.r[r] = load16(rv, (uint32_t)((key0 + 4 * quad + r) * D * 2 + ch * 16));
+  }
+}
+
+// Writes 4 keys x 8 dims as eight 4-key runs of V^T rows.
+template <int D>
+__device__ __forceinline__ void v_store(const VStage<D>& st, uint16_t* vt, int tid) {
+  constexpr int KCH = VStage<D>::KCH;
+  if (VStage<D>::GROUPS >= kThreads || tid < VStage<D>::GROUPS) {
+    const int ch = tid % KCH, quad = tid / KCH;
+    const int pos = 16 * (quad >> 2) + 4 * vt_pos_of_quad(quad & 3);
+    const int chunk = pos >> 3, half = pos & 7;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-#pragma unroll
-      for (int par = 0; par < 2; ++par) {
-        const int d = 8 * ch + 2 * w + par;
-        const uint32_t e0 = par ? (st.v[0][w] >> 16) : (st.v[0][w] & 0xffffu);
-        const uint32_t e1 = par ? (st.v[1][w] >> 16) : (st.v[1][w] & 0xffffu);
-        const uint32_t e2 = par ? (st.v[2][w] >> 16) : (st.v[2][w] & 0xffffu);
-        const uint32_t e3 = par ? (st.v[3][w] >> 16) : (st.v[3][w] & 0xffffu);
-        u32x2 val = {e0 | (e1 << 16), e2 | (e3 << 16)};
-        uint16_t* row = vt + d * BN;
-        *reinterpret_cast<u32x2*>(row + ((chunk ^ vt_swz(d)) << 3) + half) = val;
-      }
+      // Low and high bf16 of dword w of the four rows.
+      const uint32_t lo01 = __builtin_amdgcn_perm(st.r[1][w], st.r[0][w], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(st.r[3][w], st.r[2][w], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(st.r[1][w], st.r[0][w], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(st.r[3][w], st.r[2][w], 0x07060302u);
+      const int d0 = 8 * ch + 2 * w, d1 = d0 + 1;
+      *reinterpret_cast<u32x2*>(vt + d0 * BN + ((chunk ^ vt_swz(d0)) << 3) + half) =
+          u32x2{lo01, lo23};
+      *reinterpret_cast<u32x2*>(vt + d1 * BN + ((chunk ^ vt_swz(d1)) << 3) + half) =
+          u32x2{hi01, hi23};
     }
   }
 }
@@ -184,6 +202,7 @@ struct StageIter {
     return t < nmt ? 2 * t : -1;
   }
   __device__ int next(int st) const {
+    if (st < 0) return -1;
     const int nx = st + 1;
     if (nx * BN >= S) return -1;
     if (!row || (nx & 1)) return nx;                   // dense, or the second half of a mask tile
@@ -191,18 +210,41 @@ struct StageIter {
   }
 };
 
-template <int D, StoreMode MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+// S^T (two 32-key blocks x 32 queries) = K_stage Q^T.
+template <int D>
+__device__ __forceinline__ void qk_mfma(f32x16 (&s)[2], const uint16_t* ks,
+                                        const bf16x8 (&qf)[D / 16], int l32, int g) {
+  constexpr int NKS = D / 16;
+  bf16x8 a[2][NKS];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const uint16_t* krow = ks + (32 * mb + l32) * Smem<D>::KROW + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) a[mb][kk] = *reinterpret_cast<const bf16x8*>(krow + kk * 16);
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    s[mb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk)
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][kk], qf[kk], s[mb], 0, 0, 0);
+  }
+}
+
+template <int D, StoreMode MODE, bool NEG>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fa_fwd_kernel(FwdParams p) {
   constexpr int NKS = D / 16;     // QK^T contraction steps
   constexpr int NDB = D / 32;     // 32-dim blocks of O^T
-  constexpr int KROW = Smem<D>::KROW;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<D>::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[Smem<D>::TOTAL];
+  uint16_t* const kbuf0 = smem;
+  uint16_t* const vbuf0 = smem + 2 * Smem<D>::K_ELEMS;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const float c = p.c;
+  const float fill = NEG ? __builtin_inff() : -__builtin_inff();   // fill * c = -inf
   const uint32_t head_bytes = (uint32_t)p.S * D * 2;
 
   for (int unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
@@ -226,100 +268,157 @@ void fa_fwd_kernel(FwdParams p) {
     float m_run = -__builtin_inff();
     float l_run = 0.0f;
 
-    StageIter it{p.mask ? p.mask + ((size_t)h * p.nmt + qt) * p.mw : nullptr, p.S, p.nmt, p.mw};
-    int st = it.first();
-    Stage<D> regs;
-    if (st >= 0) {
-      stage_load<D>(regs, rk, rv, st * BN, tid);
-      stage_store<D>(regs, smem, smem + Smem<D>::K_ELEMS, tid);
+    const StageIter it{p.mask ? p.mask + ((size_t)h * p.nmt + qt) * p.mw : nullptr, p.S, p.nmt,
+                       p.mw};
+    int st0 = it.first();
+    int st1 = it.next(st0);
+
+    // Prologue: K and V of the first stage, K of the second, scores of the first.
+    f32x16 s_cur[2] = {f32x16{}, f32x16{}};
+    KStage<D> kreg;
+    VStage<D> vreg;
+    if (st0 >= 0) {
+      k_load<D>(kreg, rk, st0 * BN, tid);
+      v_load<D>(vreg, rv, st0 * BN, tid);
+      k_store<D>(kreg, kbuf0, tid);
+      v_store<D>(vreg, vbuf0, tid);
+      if (st1 >= 0) {
+        k_load<D>(kreg, rk, st1 * BN, tid);
+        k_store<D>(kreg, kbuf0 + Smem<D>::K_ELEMS, tid);
+      }
     }
     __syncthreads();
-    int buf = 0;
-    while (st >= 0) {
-      const int nx = it.next(st);
-      if (nx >= 0) stage_load<D>(regs, rk, rv, nx * BN, tid);
-      const uint16_t* ks_lds = smem + buf * Smem<D>::STAGE;
-      const uint16_t* vt_lds = ks_lds + Smem<D>::K_ELEMS;
+    if (st0 >= 0) qk_mfma<D>(s_cur, kbuf0, qf, l32, g);
+    __syncthreads();   // every wave is done with K buffer 0 before it is refilled
 
-      // ---- S^T = K Q^T: two 32-key blocks.
-      f32x16 s[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16{};
-        const uint16_t* krow = ks_lds + (32 * mb + l32) * KROW + g * 8;
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + kk * 16);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mb], 0, 0, 0);
-        }
-      }
+    // One K/V stage, software-pipelined: region A computes the softmax of the
+    // current scores (sc) while the MFMAs produce the next stage's scores (sn);
+    // region B runs PV of the current stage and stages the following K/V
+    // tiles into LDS.  Called with the two score tiles alternating so that no
+    // copy between them is needed.
+    int n = 0;   // sequence number of the current stage (buffer parity)
+    auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      const int st2 = it.next(st1);
+      // Global loads for the stages after this one: K two ahead, V one ahead.
+      // A stage that does not exist is read at offset S, which the buffer
+      // resource returns as zeros; its LDS copy is never used.
+      k_load<D>(kreg, rk, (st2 >= 0 ? st2 * BN : p.S), tid);
+      v_load<D>(vreg, rv, (st1 >= 0 ? st1 * BN : p.S), tid);
 
-      // ---- online softmax for this lane's query over its 32 keys of the stage.
-      const bool tail = (st + 1) * BN > p.S;
-      const int key0 = st * BN + 4 * g;
-      if (tail) {
-        const float fill = (c >= 0.0f) ? -__builtin_inff() : __builtin_inff();
+      if ((st0 + 1) * BN > p.S) {      // ragged last stage: keys >= S do not exist
+        const int key0 = st0 * BN + 4 * g;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (key0 + 32 * mb + 8 * (r >> 2) + (r & 3) >= p.S) s[mb][r] = fill;
+            if (key0 + 32 * mb + 8 * (r >> 2) + (r & 3) >= p.S) sc[mb][r] = fill;
       }
-      float ext;
-      if (c >= 0.0f) {
-        ext = fmaxf(s[0][0], s[1][0]);
+
+      // ---- region A.  After the last stage the QK^T MFMAs read a stale K
+      // buffer and their result is dropped, which keeps the region branch-free.
+      const uint16_t* kn = kbuf0 + ((n + 1) & 1) * Smem<D>::K_ELEMS + l32 * Smem<D>::KROW + g * 8;
+      const uint16_t* vt = vbuf0 + (n & 1) * Smem<D>::V_ELEMS;
+      constexpr int NA = 2 * NKS;                  // QK^T MFMAs of the next stage
+      constexpr int NB = 4 * NDB;                  // PV MFMAs of this stage
+      constexpr int KLEAD = 3;                     // K operand reads issued ahead
+      constexpr int VLEAD = 4;                     // V operand reads issued ahead
+      constexpr int NMAX = NA >= 16 ? 2 : 1;       // segments reducing the row extreme
+      constexpr int NEXP = NA - NMAX - 2;          // segments of exp2 pairs
+      // MFMA i of region A: key block i & 1, dims 16 * (i >> 1).
+      auto ka_read = [&](int i) {
+        return *reinterpret_cast<const bf16x8*>(kn + (i & 1) * 32 * Smem<D>::KROW + (i >> 1) * 16);
+      };
+      // MFMA j of region B: key step j / NDB, dim block j % NDB.
+      auto va_read = [&](int j) {
+        const int kk = j / NDB, db = j % NDB;
+        const int d = 32 * db + l32;
+        return *reinterpret_cast<const bf16x8*>(vt + d * BN + (((2 * kk + g) ^ vt_swz(d)) << 3));
+      };
+      bf16x8 ka[NA];
+      bf16x8 va[NB];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) ext = fmaxf(ext, fmaxf(s[0][r], s[1][r]));
-        ext = halves_max(ext);
-      } else {
-        ext = fminf(s[0][0], s[1][0]);
+      for (int i = 0; i < KLEAD; ++i) ka[i] = ka_read(i);
+      sn[0] = f32x16{};
+      sn[1] = f32x16{};
+      float e0 = 0.0f, e1 = 0.0f, neg_m = 0.0f, alpha = 1.0f, lsum = 0.0f;
+      bool rescale = false;
+      uint32_t pk[16];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) ext = fminf(ext, fminf(s[0][r], s[1][r]));
-        ext = halves_min(ext);
+      for (int seg = 0; seg < NA; ++seg) {
+        if (seg + KLEAD < NA) ka[seg + KLEAD] = ka_read(seg + KLEAD);
+        if (seg >= NA - VLEAD) va[seg - (NA - VLEAD)] = va_read(seg - (NA - VLEAD));
+        sn[seg & 1] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[seg], qf[seg >> 1], sn[seg & 1], 0, 0, 0);
+        if (seg < NMAX) {
+          // Row extreme of this lane's keys (max for c > 0, min for c < 0).
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            if (NMAX == 2 && mb != seg) continue;
+            float e = sc[mb][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) e = NEG ? fminf(e, sc[mb][r]) : fmaxf(e, sc[mb][r]);
+            if (mb == 0) e0 = e; else e1 = e;
+          }
+        } else if (seg == NMAX) {
+          float e = NEG ? fminf(e0, e1) : fmaxf(e0, e1);
+          e = NEG ? halves_min(e) : halves_max(e);
+          const float m_cand = fmaxf(m_run, e * c);
+          rescale = __builtin_amdgcn_ballot_w64(m_cand > m_run + kTau) != 0;
+          const float m_use = rescale ? m_cand : m_run;
+          alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+          m_run = m_use;
+          neg_m = -m_use;
+        } else if (seg < NMAX + 1 + NEXP) {
+          const int k = seg - NMAX - 1;
+#pragma unroll
+          for (int pi = (16 * k) / NEXP; pi < (16 * (k + 1)) / NEXP; ++pi) {
+            const int mb = pi >> 3, r = 2 * (pi & 7);
+            const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r], c, neg_m));
+            const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r + 1], c, neg_m));
+            lsum += x0;
+            lsum += x1;
+            pk[pi] = pack_bf16(x0, x1);
+            // Pin the value here: keeps the exp2 work inside this segment
+            // instead of letting it sink past the rescale branch below.
+            asm volatile("" ::"v"(pk[pi]));
+          }
+        } else {
+          l_run = l_run * alpha + lsum;
+          asm volatile("" ::"v"(l_run));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const float m_new = fmaxf(m_run, ext * c);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run + kTau) != 0) {
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+
+      // ---- region B: PV of this stage, then LDS staging of the next stages.
+      if (rescale) {
 #pragma unroll
         for (int i = 0; i < NDB; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
       }
-      bf16x8 pb[4];
-      float lsum = 0.0f;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = exp2f(__builtin_fmaf(s[mb][r], c, -m_run));
-          if (tail && key0 + 32 * mb + 8 * (r >> 2) + (r & 3) >= p.S) x = 0.0f;
-          lsum += x;
-          pb[2 * mb + (r >> 3)][r & 7] = (__bf16)x;
-        }
+      for (int j = 0; j < NB; ++j) {
+        if (j + VLEAD < NB) va[j + VLEAD] = va_read(j + VLEAD);
+        const int kk = j / NDB, db = j % NDB;
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, u32x4{pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]});
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb, acc[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      l_run += lsum;
-
-      // ---- O^T += V^T P^T: four 16-key steps per 32-dim block.
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + l32;
-        const uint16_t* vrow = vt_lds + d * BN;
-        const int sw = vt_swz(d);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + (((2 * kk + g) ^ sw) << 3));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], acc[db], 0, 0, 0);
-        }
-      }
-
-      if (nx >= 0)
-        stage_store<D>(regs, smem + (buf ^ 1) * Smem<D>::STAGE,
-                       smem + (buf ^ 1) * Smem<D>::STAGE + Smem<D>::K_ELEMS, tid);
+      k_store<D>(kreg, kbuf0 + (n & 1) * Smem<D>::K_ELEMS, tid);
+      v_store<D>(vreg, vbuf0 + ((n + 1) & 1) * Smem<D>::V_ELEMS, tid);
       __syncthreads();
-      buf ^= 1;
-      st = nx;
+
+      st0 = st1;
+      st1 = st2;
+      ++n;
+    };
+
+    f32x16 s_alt[2];
+    while (st0 >= 0) {
+      step(s_cur, s_alt);
+      if (st0 < 0) break;
+      step(s_alt, s_cur);
     }
 
     // ---- epilogue: normalise, round to bf16, store 8 consecutive dims per lane.
@@ -345,25 +444,24 @@ void fa_fwd_kernel(FwdParams p) {
           const uint32_t b1 = pack_bf16(acc[db][r0 + 6] * inv, acc[db][r0 + 7] * inv);
           const Pair x = swap_halves(a0, b0);
           const Pair y = swap_halves(a1, b1);
-          const u32x4 val = {x.lo, y.lo, x.hi, y.hi};
-          *reinterpret_cast<u32x4*>(dst + 32 * db + 16 * hf + 8 * g) = val;
+          *reinterpret_cast<u32x4*>(dst + 32 * db + 16 * hf + 8 * g) = u32x4{x.lo, y.lo, x.hi, y.hi};
         }
       }
     }
   }
 }
 
-template <int D, StoreMode MODE>
+template <int D, StoreMode MODE, bool NEG>
 static int launch_one(const FwdParams& p, int grid_cap, hipStream_t stream) {
   const int grid = p.units < grid_cap ? p.units : grid_cap;
-  hipLaunchKernelGGL((fa_fwd_kernel<D, MODE>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, MODE, NEG>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <int D, StoreMode MODE>
 static int occupancy_one(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fa_fwd_kernel<D, MODE>, kThreads, 0)
-                 == hipSuccess ? 0 : -1;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fa_fwd_kernel<D, MODE, false>,
+                                                      kThreads, 0) == hipSuccess ? 0 : -1;
 }
 
 int kernel_occupancy(int D, StoreMode mode, int* blocks_per_cu) {
@@ -374,11 +472,17 @@ int kernel_occupancy(int D, StoreMode mode, int* blocks_per_cu) {
   return -1;
 }
 
+template <int D, StoreMode MODE>
+static int launch_sign(const FwdParams& p, int grid_cap, hipStream_t stream) {
+  return p.c < 0.0f ? launch_one<D, MODE, true>(p, grid_cap, stream)
+                    : launch_one<D, MODE, false>(p, grid_cap, stream);
+}
+
 int launch_fwd(int D, StoreMode mode, const FwdParams& p, int grid_cap, hipStream_t stream) {
-  if (D == 128) return mode == StoreMode::Slab ? launch_one<128, StoreMode::Slab>(p, grid_cap, stream)
-                                               : launch_one<128, StoreMode::Plain>(p, grid_cap, stream);
-  if (D == 64) return mode == StoreMode::Slab ? launch_one<64, StoreMode::Slab>(p, grid_cap, stream)
-                                              : launch_one<64, StoreMode::Plain>(p, grid_cap, stream);
+  if (D == 128) return mode == StoreMode::Slab ? launch_sign<128, StoreMode::Slab>(p, grid_cap, stream)
+                                               : launch_sign<128, StoreMode::Plain>(p, grid_cap, stream);
+  if (D == 64) return mode == StoreMode::Slab ? launch_sign<64, StoreMode::Slab>(p, grid_cap, stream)
+                                              : launch_sign<64, StoreMode::Plain>(p, grid_cap, stream);
   return -1;
 }
 
