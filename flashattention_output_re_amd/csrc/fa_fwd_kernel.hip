@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_fwd_kernel.h"
 
 namespace fa {
@@ -51,6 +53,15 @@ constexpr int kThreads = 256;
 constexpr int BM = 128;          // queries per output tile (= mask tile)
 constexpr int BN = 64;           // keys per LDS stage
 constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
+#ifndef FA_KLEAD
+#define FA_KLEAD 3
+#endif
+#ifndef FA_VLEAD
+#define FA_VLEAD 4
+#endif
+#ifndef FA_WAVES_PER_EU
+#define FA_WAVES_PER_EU 1
+#endif
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
 
@@ -93,92 +104,48 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Position of key j (0..15 within its 16-key group) in the V^T LDS row: the
-// middle two 4-key blocks trade places, so that positions 8g..8g+7 hold the
-// keys {0-3, 8-11} (g = 0) and {4-7, 12-15} (g = 1) the MFMA B operand uses.
-__device__ __forceinline__ int vt_pos_of_quad(int quad16) {   // quad16 = (j % 16) / 4
-  return (quad16 == 1) ? 2 : (quad16 == 2) ? 1 : quad16;
-}
-// XOR swizzle of the 16-byte chunks of a V^T row (8 chunks per 64-key row).
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) ^ d) & 7; }
-
-template <int D>
-struct Smem {
-  static constexpr int KROW = D + 8;                 // padded K row, elements
-  static constexpr int K_ELEMS = BN * KROW;          // one K stage
-  static constexpr int V_ELEMS = D * BN;             // one V^T stage
-  static constexpr int TOTAL = 2 * K_ELEMS + 2 * V_ELEMS;
+// K and V stages live in LDS row-major (one key per row, D bf16 = D/8 16-byte
+// chunks), filled straight from global memory by buffer_load ... lds (lane l
+// of a wave instruction writes the 16 bytes at M0 + 16 l).  Chunk c of row r
+// sits at chunk position c ^ swz(r), which keeps the MFMA operand reads free
+// of bank conflicts.
+template <int D> struct Tile {
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int ELEMS = BN * D;               // bf16 per stage
+  static constexpr int TOTAL = 4 * ELEMS;            // K and V, double buffered
 };
+// K rows are read 16 at a time at one logical chunk: XOR with the row's low bits.
+template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Tile<D>::CH - 1); }
+// V is read by ds_read_b64_tr_b16: 4 consecutive rows at 2 consecutive chunks
+// per 16 lanes; XOR the chunk by 4 * (row % 4).
+template <int D> __device__ __forceinline__ int v_swz(int r) { return (4 * (r & 3)) & (Tile<D>::CH - 1); }
 
-template <int D>
-struct KStage {
-  static constexpr int KCH = D / 8;                      // 16 B chunks per row
-  static constexpr int PER_T = BN * KCH / kThreads;      // chunks per thread
-  u32x4 r[PER_T];
-};
-
-template <int D>
-struct VStage {
-  static constexpr int KCH = D / 8;
-  static constexpr int GROUPS = (BN / 4) * KCH;          // 4 keys x 8 dims per group
-  u32x4 r[4];
-};
-
-template <int D>
-__device__ __forceinline__ void k_load(KStage<D>& st, __amdgpu_buffer_rsrc_t rk, int key0, int tid) {
-  constexpr int KCH = KStage<D>::KCH;
+// One K (SWZ_V = false) or V (true) stage of BN keys starting at key0 into
+// `buf`; keys past S come back as zeros.  Each wave issues CH/4 instructions.
+template <int D, bool SWZ_V>
+__device__ __forceinline__ void stage_dma(uint16_t* buf, __amdgpu_buffer_rsrc_t r, int key0,
+                                          int wave, int lane) {
+  constexpr int CH = Tile<D>::CH;
+  constexpr int PER_WAVE = BN * CH / (4 * 64);
 #pragma unroll
-  for (int i = 0; i < KStage<D>::PER_T; ++i) {
-    const int idx = tid + kThreads * i;
-    const int row = idx / KCH, ch = idx % KCH;
-    st.r[i] = load16(rk, (uint32_t)((key0 + row) * D * 2 + ch * 16));
+  for (int q = 0; q < PER_WAVE; ++q) {
+    const int blk = PER_WAVE * wave + q;           // 64-chunk block of the stage
+    const int pos = 64 * blk + lane;               // chunk position written by this lane
+    const int row = pos / CH, pc = pos % CH;
+    const int lc = pc ^ (SWZ_V ? v_swz<D>(row) : k_swz<D>(row));   // logical chunk
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(buf + 64 * 8 * blk), 16,
+        (uint32_t)((key0 + row) * D * 2 + lc * 16), 0, 0, 0);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void k_store(const KStage<D>& st, uint16_t* ks, int tid) {
-  constexpr int KCH = KStage<D>::KCH;
-#pragma unroll
-  for (int i = 0; i < KStage<D>::PER_T; ++i) {
-    const int idx = tid + kThreads * i;
-    const int row = idx / KCH, ch = idx % KCH;
-    *reinterpret_cast<u32x4*>(ks + row * Smem<D>::KROW + ch * 8) = st.r[i];
-  }
+__device__ __forceinline__ void wait_dma() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS DMA has landed
 }
 
-template <int D>
-__device__ __forceinline__ void v_load(VStage<D>& st, __amdgpu_buffer_rsrc_t rv, int key0, int tid) {
-  constexpr int KCH = VStage<D>::KCH;
-  if (VStage<D>::GROUPS >= kThreads || tid < VStage<D>::GROUPS) {
-    const int ch = tid % KCH, quad = tid / KCH;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      st.r[r] = load16(rv, (uint32_t)((key0 + 4 * quad + r) * D * 2 + ch * 16));
-  }
-}
-
-// Writes 4 keys x 8 dims as eight 4-key runs of V^T rows.
-template <int D>
-__device__ __forceinline__ void v_store(const VStage<D>& st, uint16_t* vt, int tid) {
-  constexpr int KCH = VStage<D>::KCH;
-  if (VStage<D>::GROUPS >= kThreads || tid < VStage<D>::GROUPS) {
-    const int ch = tid % KCH, quad = tid / KCH;
-    const int pos = 16 * (quad >> 2) + 4 * vt_pos_of_quad(quad & 3);
-    const int chunk = pos >> 3, half = pos & 7;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // Low and high bf16 of dword w of the four rows.
-      const uint32_t lo01 = __builtin_amdgcn_perm(st.r[1][w], st.r[0][w], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(st.r[3][w], st.r[2][w], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(st.r[1][w], st.r[0][w], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(st.r[3][w], st.r[2][w], 0x07060302u);
-      const int d0 = 8 * ch + 2 * w, d1 = d0 + 1;
-      *reinterpret_cast<u32x2*>(vt + d0 * BN + ((chunk ^ vt_swz(d0)) << 3) + half) =
-          u32x2{lo01, lo23};
-      *reinterpret_cast<u32x2*>(vt + d1 * BN + ((chunk ^ vt_swz(d1)) << 3) + half) =
-          u32x2{hi01, hi23};
-    }
-  }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
 // Iterates the K/V stages (BN keys each) a query tile attends to: all stages
@@ -210,35 +177,61 @@ struct StageIter {
   }
 };
 
+// A operand of S^T = K Q^T: keys 32 mb + (lane % 32), dims 16 kk + 8 (lane / 32) + [0, 8).
+template <int D>
+__device__ __forceinline__ bf16x8 k_operand(const uint16_t* kbuf, int mb, int kk, int l32, int g) {
+  const int r = 32 * mb + l32;
+  return *reinterpret_cast<const bf16x8*>(kbuf + r * D + 8 * ((2 * kk + g) ^ k_swz<D>(r)));
+}
+
+// A operand of O^T = V^T P^T for 16-key step kk and 32-dim block db: lane l
+// holds dim 32 db + l % 32 at the keys 16 kk + {0-3, 8-11} (l < 32) or
+// {4-7, 12-15} (l >= 32), the key order of the S^T accumulator.  Each
+// transposing read gives a lane 4 keys of one dim; within 16 lanes, lane j
+// points at key 4 (j / 16...)-relative row j / 4 and dims 4 (j % 4) + [0, 4).
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(const uint16_t* vbuf, int kk, int db, int lane) {
+  const int j = lane & 15, grp = lane >> 4;
+  const int dim = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
+  s16x4 h[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = 16 * kk + 8 * half + 4 * (grp >> 1) + (j >> 2);
+    h[half] = lds_read_tr(vbuf + row * D + 8 * ((dim >> 3) ^ v_swz<D>(row)) + (dim & 7));
+  }
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // S^T (two 32-key blocks x 32 queries) = K_stage Q^T.
 template <int D>
 __device__ __forceinline__ void qk_mfma(f32x16 (&s)[2], const uint16_t* ks,
                                         const bf16x8 (&qf)[D / 16], int l32, int g) {
   constexpr int NKS = D / 16;
-  bf16x8 a[2][NKS];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const uint16_t* krow = ks + (32 * mb + l32) * Smem<D>::KROW + g * 8;
-#pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) a[mb][kk] = *reinterpret_cast<const bf16x8*>(krow + kk * 16);
-  }
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     s[mb] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk)
-      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][kk], qf[kk], s[mb], 0, 0, 0);
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<D>(ks, mb, kk, l32, g), qf[kk],
+                                                      s[mb], 0, 0, 0);
   }
 }
 
 template <int D, StoreMode MODE, bool NEG>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(FA_WAVES_PER_EU, FA_WAVES_PER_EU)))
 void fa_fwd_kernel(FwdParams p) {
   constexpr int NKS = D / 16;     // QK^T contraction steps
   constexpr int NDB = D / 32;     // 32-dim blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t smem[Smem<D>::TOTAL];
-  uint16_t* const kbuf0 = smem;
-  uint16_t* const vbuf0 = smem + 2 * Smem<D>::K_ELEMS;
+  // Four separate LDS objects (K and V, double buffered) so that the compiler
+  // can tell a DMA into one buffer from reads of another and does not wait
+  // for the DMA before those reads.
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t kb1[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t vb0[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t vb1[Tile<D>::ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -275,20 +268,14 @@ void fa_fwd_kernel(FwdParams p) {
 
     // Prologue: K and V of the first stage, K of the second, scores of the first.
     f32x16 s_cur[2] = {f32x16{}, f32x16{}};
-    KStage<D> kreg;
-    VStage<D> vreg;
     if (st0 >= 0) {
-      k_load<D>(kreg, rk, st0 * BN, tid);
-      v_load<D>(vreg, rv, st0 * BN, tid);
-      k_store<D>(kreg, kbuf0, tid);
-      v_store<D>(vreg, vbuf0, tid);
-      if (st1 >= 0) {
-        k_load<D>(kreg, rk, st1 * BN, tid);
-        k_store<D>(kreg, kbuf0 + Smem<D>::K_ELEMS, tid);
-      }
+      stage_dma<D, false>(kb0, rk, st0 * BN, wave, lane);
+      stage_dma<D, true>(vb0, rv, st0 * BN, wave, lane);
+      if (st1 >= 0) stage_dma<D, false>(kb1, rk, st1 * BN, wave, lane);
     }
+    wait_dma();
     __syncthreads();
-    if (st0 >= 0) qk_mfma<D>(s_cur, kbuf0, qf, l32, g);
+    if (st0 >= 0) qk_mfma<D>(s_cur, kb0, qf, l32, g);
     __syncthreads();   // every wave is done with K buffer 0 before it is refilled
 
     // One K/V stage, software-pipelined: region A computes the softmax of the
@@ -296,14 +283,22 @@ void fa_fwd_kernel(FwdParams p) {
     // region B runs PV of the current stage and stages the following K/V
     // tiles into LDS.  Called with the two score tiles alternating so that no
     // copy between them is needed.
-    int n = 0;   // sequence number of the current stage (buffer parity)
-    auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    // PAR is the parity of the stage's sequence number: stage n reads K of
+    // the next stage from kb[(n + 1) % 2] and V from vb[n % 2], and refills
+    // kb[n % 2] (K two ahead) and vb[(n + 1) % 2] (V one ahead).
+    auto step = [&](auto PAR, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      constexpr int par = decltype(PAR)::value;
+      uint16_t* const k_fill = par ? kb1 : kb0;
+      const uint16_t* const kn = par ? kb0 : kb1;
+      uint16_t* const v_fill = par ? vb0 : vb1;
+      const uint16_t* const vt = par ? vb1 : vb0;
       const int st2 = it.next(st1);
-      // Global loads for the stages after this one: K two ahead, V one ahead.
-      // A stage that does not exist is read at offset S, which the buffer
-      // resource returns as zeros; its LDS copy is never used.
-      k_load<D>(kreg, rk, (st2 >= 0 ? st2 * BN : p.S), tid);
-      v_load<D>(vreg, rv, (st1 >= 0 ? st1 * BN : p.S), tid);
+      // LDS DMA for the stages after this one, into the buffers the previous
+      // stage freed: K two ahead, V one ahead.  A stage that does not exist is
+      // read at key S, which the buffer resource returns as zeros; its LDS
+      // copy is never used.
+      stage_dma<D, false>(k_fill, rk, (st2 >= 0 ? st2 * BN : p.S), wave, lane);
+      stage_dma<D, true>(v_fill, rv, (st1 >= 0 ? st1 * BN : p.S), wave, lane);
 
       if ((st0 + 1) * BN > p.S) {      // ragged last stage: keys >= S do not exist
         const int key0 = st0 * BN + 4 * g;
@@ -316,24 +311,16 @@ void fa_fwd_kernel(FwdParams p) {
 
       // ---- region A.  After the last stage the QK^T MFMAs read a stale K
       // buffer and their result is dropped, which keeps the region branch-free.
-      const uint16_t* kn = kbuf0 + ((n + 1) & 1) * Smem<D>::K_ELEMS + l32 * Smem<D>::KROW + g * 8;
-      const uint16_t* vt = vbuf0 + (n & 1) * Smem<D>::V_ELEMS;
       constexpr int NA = 2 * NKS;                  // QK^T MFMAs of the next stage
       constexpr int NB = 4 * NDB;                  // PV MFMAs of this stage
-      constexpr int KLEAD = 3;                     // K operand reads issued ahead
-      constexpr int VLEAD = 4;                     // V operand reads issued ahead
+      constexpr int KLEAD = FA_KLEAD;              // K operand reads issued ahead
+      constexpr int VLEAD = FA_VLEAD;              // V operand reads issued ahead
       constexpr int NMAX = NA >= 16 ? 2 : 1;       // segments reducing the row extreme
       constexpr int NEXP = NA - NMAX - 2;          // segments of exp2 pairs
       // MFMA i of region A: key block i & 1, dims 16 * (i >> 1).
-      auto ka_read = [&](int i) {
-        return *reinterpret_cast<const bf16x8*>(kn + (i & 1) * 32 * Smem<D>::KROW + (i >> 1) * 16);
-      };
+      auto ka_read = [&](int i) { return k_operand<D>(kn, i & 1, i >> 1, l32, g); };
       // MFMA j of region B: key step j / NDB, dim block j % NDB.
-      auto va_read = [&](int j) {
-        const int kk = j / NDB, db = j % NDB;
-        const int d = 32 * db + l32;
-        return *reinterpret_cast<const bf16x8*>(vt + d * BN + (((2 * kk + g) ^ vt_swz(d)) << 3));
-      };
+      auto va_read = [&](int j) { return v_operand<D>(vt, j / NDB, j % NDB, lane); };
       bf16x8 ka[NA];
       bf16x8 va[NB];
 #pragma unroll
@@ -405,20 +392,18 @@ void fa_fwd_kernel(FwdParams p) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb, acc[db], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      k_store<D>(kreg, kbuf0 + (n & 1) * Smem<D>::K_ELEMS, tid);
-      v_store<D>(vreg, vbuf0 + ((n + 1) & 1) * Smem<D>::V_ELEMS, tid);
+      wait_dma();
       __syncthreads();
 
       st0 = st1;
       st1 = st2;
-      ++n;
     };
 
     f32x16 s_alt[2];
     while (st0 >= 0) {
-      step(s_cur, s_alt);
+      step(std::integral_constant<int, 0>{}, s_cur, s_alt);
       if (st0 < 0) break;
-      step(s_alt, s_cur);
+      step(std::integral_constant<int, 1>{}, s_alt, s_cur);
     }
 
     // ---- epilogue: normalise, round to bf16, store 8 consecutive dims per lane.
