@@ -1,6 +1,6 @@
 // Fused FlashAttention forward + Ulysses slab store for gfx950 (MI355X).
 //
-// One persistent workgroup of 4 wavefronts per CU owns 128-query output tiles
+// Persistent workgroups of 4 wavefronts (two per CU) own 128-query output tiles
 // of one (batch, head) at a time: it streams the K/V tiles of the whole
 // sequence through LDS, runs QK^T and PV on the bf16 MFMA units with an fp32
 // online softmax, and in the epilogue stores the finished tile straight into
@@ -27,9 +27,10 @@
 // Schedule.  On gfx950 a wavefront overlaps an MFMA with the independent VALU
 // work issued after it, so each K/V stage is software-pipelined inside the
 // wave: the QK^T MFMAs of the next stage are interleaved with the softmax of
-// the current one, and the PV MFMAs of the current stage with the LDS staging
-// of the stages after it.  One wave per SIMD (512 VGPRs) holds both score
-// tiles, the Q fragments, the O accumulator and the staging registers.
+// the current one, and the PV MFMAs of the current stage follow.  K/V tiles
+// reach LDS by DMA, so the 256 VGPRs of two waves per SIMD (two workgroups
+// per CU) hold both score tiles, the Q fragments and the O accumulator; the
+// second wave on each SIMD covers the first one's LDS and barrier waits.
 //
 // Softmax runs in the log2 domain (c = scale * log2 e, p = exp2(s c - m)).
 // The running max is only raised when some row of the wave exceeds it by more
@@ -60,7 +61,7 @@ constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
 #define FA_VLEAD 4
 #endif
 #ifndef FA_WAVES_PER_EU
-#define FA_WAVES_PER_EU 1
+#define FA_WAVES_PER_EU 2
 #endif
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
