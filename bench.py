@@ -59,7 +59,8 @@ def load_traffic(workload: str):
 
 
 def cpu_baseline(name: str, target_s: float):
-    """Time the float64 oracle on a fixed sample of 128-query row blocks."""
+    """Time the float64 oracle on a fixed sample: consecutive 128-query row
+    blocks of head 0, then head 1, ..., until about target_s seconds."""
     import numpy as np
     import oracle
     import workloads as wl
@@ -71,23 +72,72 @@ def cpu_baseline(name: str, target_s: float):
         threads = len(os.sched_getaffinity(0))
     w = wl.WORKLOADS[name]
     inp = wl.make(name)
-    q, k, v = inp.f64("q")[:, :1], inp.f64("k")[:, :1], inp.f64("v")[:, :1]
-    mask = None if inp.mask is None else inp.mask[:1]
-    blocks = 0
+    q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
+    nblk = (w.S + 127) // 128
+    done_rows, blocks, heads = 0, 0, set()
     t0 = time.perf_counter()
-    while True:
-        rows = np.arange(128 * blocks, min(w.S, 128 * blocks + 128))
-        oracle.attention(q, k, v, w.scale, mask, rows=rows)
-        blocks += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or 128 * blocks >= w.S:
+    el = 0.0
+    for h in range(w.H):
+        mask = None if inp.mask is None else inp.mask[h:h + 1]
+        for i in range(nblk):
+            rows = np.arange(128 * i, min(w.S, 128 * i + 128))
+            oracle.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], w.scale, mask, rows=rows)
+            done_rows += len(rows)
+            blocks += 1
+            heads.add(h)
+            el = time.perf_counter() - t0
+            if el >= target_s:
+                break
+        if el >= target_s:
             break
-    n_rows = min(w.S, 128 * blocks)
-    flop = 4.0 * w.B * n_rows * w.S * w.D      # oracle scores every key (masked ones too)
+    flop = 4.0 * w.B * done_rows * w.S * w.D     # the oracle scores every key, masked ones too
     return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{name}: head 0, query rows 0..{n_rows - 1} ({blocks} blocks of 128) "
-                      f"against all {w.S} keys, float64 numpy, {el:.1f} s"}
+            "sample": f"{name}: {blocks} blocks of 128 query rows ({done_rows} rows, heads "
+                      f"{min(heads)}-{max(heads)}) against all {w.S} keys, float64 numpy, "
+                      f"{el:.1f} s"}
+
+
+def copy_calibration(mib: int):
+    """One device copy of a known size: the HBM-traffic counters read for it
+    calibrate FETCH_SIZE / WRITE_SIZE (bytes moved = mib MiB each way)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def summarize(kind: str, path: str):
+    """Print a short text summary of rocprofv3 CSV output under `path`."""
+    import csv
+    import glob
+    import statistics
+    if kind == "trace":
+        files = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+        for f in files:
+            rows = list(csv.DictReader(open(f)))
+            print(f"# {os.path.relpath(f, path)}")
+            print("| kernel | calls | total ns | average ns | min ns | max ns | % |")
+            print("|---|---|---|---|---|---|---|")
+            for r in rows:
+                print(f"| {r['Name']} | {r['Calls']} | {r['TotalDurationNs']} | "
+                      f"{float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
+                      f"{float(r['Percentage']):.2f} |")
+    else:
+        files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+        per = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                key = (r["Kernel_Name"], r["Counter_Name"])
+                per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+                per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        print("| kernel | counter | dispatches | mean per dispatch |")
+        print("|---|---|---|---|")
+        for (kname, cname), d in sorted(per.items()):
+            print(f"| {kname} | {cname} | {len(d)} | {statistics.mean(d.values()):.6g} |")
 
 
 def main():
@@ -99,7 +149,14 @@ def main():
     ap.add_argument("--overhead-pairs", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB")
+    ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIR"),
+                    help="print a summary of rocprofv3 CSV output (KIND: trace|counters)")
     a = ap.parse_args()
+    if a.summarize:
+        summarize(*a.summarize)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -204,6 +261,8 @@ def main():
                      "mean_launch_ms": round(mean_launch_ms, 4)},
         "kernel_source_sha256_16": kernel_source_hash(),
     }
+    if a.copy_calibration_mib:
+        copy_calibration(a.copy_calibration_mib)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -21,7 +21,7 @@ ARCH = "gfx950"
 # hipcc must not emit packed fp32 VALU ops (v_pk_fma_f32 and friends).  The
 # device code never tests for NaN, so max/min need no NaN canonicalisation.
 HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Xarch_device", "-fno-honor-nans",
+             "-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-fno-signed-zeros",
              # MFMA accumulators in VGPRs: the softmax reads the score tile
              # every stage, and AGPR-form MFMAs would copy it across.
              "-mllvm", "-amdgpu-mfma-vgpr-form"]
