@@ -28,8 +28,9 @@ int validate(const void* q, const void* k, const void* v, const void* out, int B
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return FA_EALIGN;
   if (mask && !aligned(mask, 8)) return FA_EALIGN;
-  // Per-head slices are addressed with 32-bit byte offsets.
-  if ((int64_t)S * D * 2 > (int64_t)INT32_MAX) return FA_ERANGE;
+  // Per-head slices are addressed with 32-bit byte offsets, which run up to
+  // one 256-query tile past the last row.
+  if (((int64_t)S + 256) * D * 2 > (int64_t)INT32_MAX) return FA_ERANGE;
   const int64_t nqt = (S + kQTile - 1) / kQTile;
   if ((int64_t)B * H * nqt > (int64_t)INT32_MAX) return FA_ERANGE;
   if ((int64_t)H * nqt * ((nqt + 63) / 64) > ((int64_t)1 << 40)) return FA_ERANGE;
@@ -38,15 +39,15 @@ int validate(const void* q, const void* k, const void* v, const void* out, int B
 
 struct DeviceGeom {
   int cus = 0;
-  int occ[2][2] = {{0, 0}, {0, 0}};   // [D == 128][mode]
+  int occ[2][2][3] = {};   // [D == 128][mode][variant]
 };
 
 std::mutex g_geom_mutex;
 DeviceGeom g_geom[kMaxDevices];
 
-// Persistent grid size for (D, mode) on the current device: every resident
-// workgroup slot of the chip, or -1 if the device cannot be queried.
-int grid_cap_for(int D, fa::StoreMode mode) {
+// Persistent grid size for (D, mode, var) on the current device: every
+// resident workgroup slot of the chip, or -1 if the device cannot be queried.
+int grid_cap_for(int D, fa::StoreMode mode, fa::Variant var) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
   std::lock_guard<std::mutex> lock(g_geom_mutex);
@@ -58,10 +59,10 @@ int grid_cap_for(int D, fa::StoreMode mode) {
       return -1;
     gm.cus = cus;
   }
-  int& occ = gm.occ[D == 128][(int)mode];
+  int& occ = gm.occ[D == 128][(int)mode][(int)var];
   if (occ == 0) {
     int blocks = 0;
-    if (fa::kernel_occupancy(D, mode, &blocks) != 0 || blocks <= 0) return -1;
+    if (fa::kernel_occupancy(D, mode, var, &blocks) != 0 || blocks <= 0) return -1;
     occ = blocks;
   }
   return gm.cus * occ;
@@ -71,7 +72,10 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
         int S, int D, int P, float scale, const uint64_t* mask, hipStream_t stream) {
   const int st = validate(q, k, v, out, B, H, S, D, P, scale, mask);
   if (st != FA_OK) return st;
-  const int cap = grid_cap_for(D, mode);
+  // Dense attention runs on the 8-wave ping-pong kernel; a block mask gives
+  // each 128-query tile its own key set, so it runs on the 4-wave kernel.
+  const fa::Variant var = mask ? fa::Variant::Quad : fa::Variant::PingPong;
+  const int cap = grid_cap_for(D, mode, var);
   if (cap <= 0) return FA_EDEVICE;
   fa::FwdParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -84,16 +88,38 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   p.S = S;
   p.P = P;
   p.Sp = S / P;
-  p.nqt = (S + kQTile - 1) / kQTile;
+  const int rows = fa::tile_rows(var);
+  p.nqt = (S + rows - 1) / rows;
   p.units = B * H * p.nqt;
-  p.nmt = p.nqt;
+  p.unit_base = 0;
+  p.nmt = (S + kQTile - 1) / kQTile;
   p.mw = (p.nmt + 63) / 64;
   p.c = (float)((double)scale * 1.4426950408889634073599246810019);
   // With c == 0 every score weighs exp2(0) = 1; any positive c small enough
   // that |s| * c rounds away against 1 gives the same weights bit for bit,
   // and keeps (-inf) * c = -inf for the keys past S.
   if (p.c == 0.0f) p.c = 1e-30f;
-  return fa::launch_fwd(D, mode, p, cap, stream) == 0 ? FA_OK : FA_ELAUNCH;
+  if (var == fa::Variant::Quad)
+    return fa::launch_fwd(D, mode, var, p, cap, stream) == 0 ? FA_OK : FA_ELAUNCH;
+
+  // Dense: whole 256-query tiles fill `cap` CUs per round.  When the last
+  // round would keep at most half of the CUs busy, its R tiles run instead as
+  // 2R half-tiles with the keys split inside each workgroup (about half the
+  // time of a whole tile), in a second launch on the same stream.
+  const int tail = p.units % cap;
+  const int stages = (S + 63) / 64;
+  if (tail == 0 || 2 * tail > cap || stages < 2)
+    return fa::launch_fwd(D, mode, var, p, cap, stream) == 0 ? FA_OK : FA_ELAUNCH;
+  const int split_cap = grid_cap_for(D, mode, fa::Variant::PingPongSplit);
+  if (split_cap <= 0) return FA_EDEVICE;
+  fa::FwdParams whole = p;
+  whole.units = p.units - tail;
+  if (whole.units > 0 && fa::launch_fwd(D, mode, var, whole, cap, stream) != 0) return FA_ELAUNCH;
+  fa::FwdParams half = p;
+  half.units = 2 * tail;
+  half.unit_base = p.units - tail;
+  return fa::launch_fwd(D, mode, fa::Variant::PingPongSplit, half, split_cap, stream) == 0
+             ? FA_OK : FA_ELAUNCH;
 }
 
 int finish_blocking(int st) {

@@ -7,6 +7,14 @@ namespace fa {
 
 enum class StoreMode : int { Slab = 0, Plain = 1 };
 
+// Workgroup shapes.  Quad: 4 waves own 128 queries, two workgroups per CU,
+// any mask.  PingPong: 8 waves own 256 queries and share one K/V stream, one
+// workgroup per CU, dense attention only.  PingPongSplit: the same 8 waves own
+// one 128-query half of a 256-query tile and split its keys between the two
+// wave groups (for the last, partial round of a dense launch).
+enum class Variant : int { Quad = 0, PingPong = 1, PingPongSplit = 2 };
+constexpr int tile_rows(Variant v) { return v == Variant::Quad ? 128 : 256; }
+
 // Kernel arguments, passed by value.  Every tensor is bf16 stored as uint16_t.
 struct FwdParams {
   const uint16_t* q;     // [B][H][S][D]
@@ -15,16 +23,18 @@ struct FwdParams {
   uint16_t* out;         // slabs [P][B][S/P][H][D] or plain [B][H][S][D]
   const uint64_t* mask;  // [H][nmt][mw] keep bits, or nullptr
   int B, H, S, P, Sp;    // Sp = S / P
-  int nqt;               // 128-query output tiles per (b, h)
-  int units;             // B * H * nqt output tiles
+  int nqt;               // output tiles (tile_rows queries) per (b, h)
+  int units;             // work units of this launch (see unit_base)
+  int unit_base;         // PingPongSplit: unit u is half u % 2 of tile unit_base + u / 2
   int nmt;               // 128-key mask tiles per row (= nqt)
   int mw;                // 64-bit words per mask row
   float c;               // scale * log2(e)
 };
 
 // Launch with at most `grid_cap` persistent workgroups; 0 on success.
-int launch_fwd(int D, StoreMode mode, const FwdParams& p, int grid_cap, hipStream_t stream);
-// Resident workgroups per CU for the instance (D, mode); 0 on success.
-int kernel_occupancy(int D, StoreMode mode, int* blocks_per_cu);
+int launch_fwd(int D, StoreMode mode, Variant var, const FwdParams& p, int grid_cap,
+               hipStream_t stream);
+// Resident workgroups per CU for the instance (D, mode, var); 0 on success.
+int kernel_occupancy(int D, StoreMode mode, Variant var, int* blocks_per_cu);
 
 }  // namespace fa

@@ -144,6 +144,17 @@ __device__ __forceinline__ void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS DMA has landed
 }
 
+// Workgroup barrier without the release/acquire fence of __syncthreads(): the
+// fence would wait for every LDS DMA still in flight.  Every LDS read issued
+// before it has been consumed by then (the MFMAs that use them precede it);
+// the empty asm statements keep the compiler from moving memory operations
+// across it.
+__device__ __forceinline__ void barrier_keep_dma() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
@@ -217,6 +228,115 @@ __device__ __forceinline__ void qk_mfma(f32x16 (&s)[2], const uint16_t* ks,
     for (int kk = 0; kk < NKS; ++kk)
       s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<D>(ks, mb, kk, l32, g), qf[kk],
                                                       s[mb], 0, 0, 0);
+  }
+}
+
+// Online softmax of one K/V stage, cut into NA pieces that interleave with
+// the NA MFMAs of the region it runs in (piece `seg` follows MFMA `seg`).
+// This lane holds 32 scores of its query (two 32-key blocks x 16).  Pieces
+// [0, NMAX) reduce the row extreme (max for c > 0, min for c < 0), piece NMAX
+// updates the running max, the next NEXP pieces compute the probabilities
+// exp2(s c - m) as bf16 pairs (the B operand of the PV MFMAs) and their sum,
+// and the last piece folds that sum into the running row sum.  The running
+// max is raised only when some row of the wave exceeds it by more than kTau.
+template <bool NEG, int NA>
+struct StageSoftmax {
+  static constexpr int NMAX = NA >= 16 ? 2 : 1;
+  static constexpr int NEXP = NA - NMAX - 2;
+  float e0 = 0.0f, e1 = 0.0f, neg_m = 0.0f, alpha = 1.0f, lsum = 0.0f;
+  bool rescale = false;
+  uint32_t pk[16];
+
+  __device__ __forceinline__ void piece(int seg, const f32x16 (&sc)[2], float c, float& m_run,
+                                        float& l_run) {
+    if (seg < NMAX) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        if (NMAX == 2 && mb != seg) continue;
+        float e = sc[mb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) e = NEG ? fminf(e, sc[mb][r]) : fmaxf(e, sc[mb][r]);
+        if (mb == 0) e0 = e; else e1 = e;
+      }
+    } else if (seg == NMAX) {
+      float e = NEG ? fminf(e0, e1) : fmaxf(e0, e1);
+      e = NEG ? halves_min(e) : halves_max(e);
+      const float m_cand = fmaxf(m_run, e * c);
+      rescale = __builtin_amdgcn_ballot_w64(m_cand > m_run + kTau) != 0;
+      const float m_use = rescale ? m_cand : m_run;
+      alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_use;
+      neg_m = -m_use;
+    } else if (seg < NMAX + 1 + NEXP) {
+      const int k = seg - NMAX - 1;
+#pragma unroll
+      for (int pi = (16 * k) / NEXP; pi < (16 * (k + 1)) / NEXP; ++pi) {
+        const int mb = pi >> 3, r = 2 * (pi & 7);
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r], c, neg_m));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r + 1], c, neg_m));
+        lsum += x0;
+        lsum += x1;
+        pk[pi] = pack_bf16(x0, x1);
+        // Pin the value here: keeps the exp2 work inside this piece instead
+        // of letting it sink past the rescale branch that follows the region.
+        asm volatile("" ::"v"(pk[pi]));
+      }
+    } else {
+      l_run = l_run * alpha + lsum;
+      asm volatile("" ::"v"(l_run));
+    }
+  }
+
+  // B operand of the PV MFMA over 16-key step kk.
+  __device__ __forceinline__ bf16x8 p_operand(int kk) const {
+    return __builtin_bit_cast(bf16x8, u32x4{pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]});
+  }
+};
+
+// Keys >= S of a ragged last stage do not exist: their scores become fill
+// (fill * c = -inf).  Lane (l32, g) holds keys 32 mb + 8 (r / 4) + 4 g + r % 4.
+__device__ __forceinline__ void mask_tail(f32x16 (&sc)[2], int stage_key0, int S, int g, float fill) {
+  if (stage_key0 + BN <= S) return;
+  const int key0 = stage_key0 + 4 * g;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (key0 + 32 * mb + 8 * (r >> 2) + (r & 3) >= S) sc[mb][r] = fill;
+}
+
+// Epilogue of one wave's 32 queries: normalise by the row sum, round to bf16
+// and store 8 consecutive dims per lane with 128-bit stores, into the slab of
+// the query's destination (Slab) or the [B][H][S][D] output (Plain).  A row
+// whose every key was masked out has l = 0 and stores zeros.
+template <int D, StoreMode MODE>
+__device__ __forceinline__ void store_tile(const FwdParams& p, const f32x16 (&acc)[D / 32],
+                                           float l_run, int qrow, int b, int h, int bh, int g) {
+  constexpr int NDB = D / 32;
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qrow >= p.S) return;
+  size_t row_off;
+  if (MODE == StoreMode::Slab) {
+    const int slab = qrow / p.Sp, t = qrow - slab * p.Sp;
+    row_off = (((size_t)slab * p.B + b) * p.Sp + t) * p.H + h;
+  } else {
+    row_off = (size_t)bh * p.S + qrow;
+  }
+  uint16_t* dst = p.out + row_off * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r0 = 8 * hf;
+      const uint32_t a0 = pack_bf16(acc[db][r0 + 0] * inv, acc[db][r0 + 1] * inv);
+      const uint32_t a1 = pack_bf16(acc[db][r0 + 2] * inv, acc[db][r0 + 3] * inv);
+      const uint32_t b0 = pack_bf16(acc[db][r0 + 4] * inv, acc[db][r0 + 5] * inv);
+      const uint32_t b1 = pack_bf16(acc[db][r0 + 6] * inv, acc[db][r0 + 7] * inv);
+      const Pair x = swap_halves(a0, b0);
+      const Pair y = swap_halves(a1, b1);
+      *reinterpret_cast<u32x4*>(dst + 32 * db + 16 * hf + 8 * g) = u32x4{x.lo, y.lo, x.hi, y.hi};
+    }
   }
 }
 
@@ -301,14 +421,7 @@ void fa_fwd_kernel(FwdParams p) {
       stage_dma<D, false>(k_fill, rk, (st2 >= 0 ? st2 * BN : p.S), wave, lane);
       stage_dma<D, true>(v_fill, rv, (st1 >= 0 ? st1 * BN : p.S), wave, lane);
 
-      if ((st0 + 1) * BN > p.S) {      // ragged last stage: keys >= S do not exist
-        const int key0 = st0 * BN + 4 * g;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key0 + 32 * mb + 8 * (r >> 2) + (r & 3) >= p.S) sc[mb][r] = fill;
-      }
+      mask_tail(sc, st0 * BN, p.S, g, fill);
 
       // ---- region A.  After the last stage the QK^T MFMAs read a stale K
       // buffer and their result is dropped, which keeps the region branch-free.
@@ -316,8 +429,6 @@ void fa_fwd_kernel(FwdParams p) {
       constexpr int NB = 4 * NDB;                  // PV MFMAs of this stage
       constexpr int KLEAD = FA_KLEAD;              // K operand reads issued ahead
       constexpr int VLEAD = FA_VLEAD;              // V operand reads issued ahead
-      constexpr int NMAX = NA >= 16 ? 2 : 1;       // segments reducing the row extreme
-      constexpr int NEXP = NA - NMAX - 2;          // segments of exp2 pairs
       // MFMA i of region A: key block i & 1, dims 16 * (i >> 1).
       auto ka_read = [&](int i) { return k_operand<D>(kn, i & 1, i >> 1, l32, g); };
       // MFMA j of region B: key step j / NDB, dim block j % NDB.
@@ -328,69 +439,29 @@ void fa_fwd_kernel(FwdParams p) {
       for (int i = 0; i < KLEAD; ++i) ka[i] = ka_read(i);
       sn[0] = f32x16{};
       sn[1] = f32x16{};
-      float e0 = 0.0f, e1 = 0.0f, neg_m = 0.0f, alpha = 1.0f, lsum = 0.0f;
-      bool rescale = false;
-      uint32_t pk[16];
+      StageSoftmax<NEG, NA> sm;
 #pragma unroll
       for (int seg = 0; seg < NA; ++seg) {
         if (seg + KLEAD < NA) ka[seg + KLEAD] = ka_read(seg + KLEAD);
         if (seg >= NA - VLEAD) va[seg - (NA - VLEAD)] = va_read(seg - (NA - VLEAD));
         sn[seg & 1] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[seg], qf[seg >> 1], sn[seg & 1], 0, 0, 0);
-        if (seg < NMAX) {
-          // Row extreme of this lane's keys (max for c > 0, min for c < 0).
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            if (NMAX == 2 && mb != seg) continue;
-            float e = sc[mb][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) e = NEG ? fminf(e, sc[mb][r]) : fmaxf(e, sc[mb][r]);
-            if (mb == 0) e0 = e; else e1 = e;
-          }
-        } else if (seg == NMAX) {
-          float e = NEG ? fminf(e0, e1) : fmaxf(e0, e1);
-          e = NEG ? halves_min(e) : halves_max(e);
-          const float m_cand = fmaxf(m_run, e * c);
-          rescale = __builtin_amdgcn_ballot_w64(m_cand > m_run + kTau) != 0;
-          const float m_use = rescale ? m_cand : m_run;
-          alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-          m_run = m_use;
-          neg_m = -m_use;
-        } else if (seg < NMAX + 1 + NEXP) {
-          const int k = seg - NMAX - 1;
-#pragma unroll
-          for (int pi = (16 * k) / NEXP; pi < (16 * (k + 1)) / NEXP; ++pi) {
-            const int mb = pi >> 3, r = 2 * (pi & 7);
-            const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r], c, neg_m));
-            const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r + 1], c, neg_m));
-            lsum += x0;
-            lsum += x1;
-            pk[pi] = pack_bf16(x0, x1);
-            // Pin the value here: keeps the exp2 work inside this segment
-            // instead of letting it sink past the rescale branch below.
-            asm volatile("" ::"v"(pk[pi]));
-          }
-        } else {
-          l_run = l_run * alpha + lsum;
-          asm volatile("" ::"v"(l_run));
-        }
+        sm.piece(seg, sc, c, m_run, l_run);
         __builtin_amdgcn_sched_barrier(0);
       }
 
       // ---- region B: PV of this stage, then LDS staging of the next stages.
-      if (rescale) {
+      if (sm.rescale) {
 #pragma unroll
         for (int i = 0; i < NDB; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc[i][r] *= sm.alpha;
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         if (j + VLEAD < NB) va[j + VLEAD] = va_read(j + VLEAD);
-        const int kk = j / NDB, db = j % NDB;
-        const bf16x8 pb = __builtin_bit_cast(
-            bf16x8, u32x4{pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]});
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb, acc[db], 0, 0, 0);
+        acc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], sm.p_operand(j / NDB),
+                                                               acc[j % NDB], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_dma();
@@ -407,69 +478,298 @@ void fa_fwd_kernel(FwdParams p) {
       step(std::integral_constant<int, 1>{}, s_alt, s_cur);
     }
 
-    // ---- epilogue: normalise, round to bf16, store 8 consecutive dims per lane.
-    const float l_tot = halves_sum(l_run);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (qrow < p.S) {
-      size_t row_off;
-      if (MODE == StoreMode::Slab) {
-        const int slab = qrow / p.Sp, t = qrow - slab * p.Sp;
-        row_off = (((size_t)slab * p.B + b) * p.Sp + t) * p.H + h;
-      } else {
-        row_off = (size_t)bh * p.S + qrow;
-      }
-      uint16_t* dst = p.out + row_off * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int r0 = 8 * hf;
-          const uint32_t a0 = pack_bf16(acc[db][r0 + 0] * inv, acc[db][r0 + 1] * inv);
-          const uint32_t a1 = pack_bf16(acc[db][r0 + 2] * inv, acc[db][r0 + 3] * inv);
-          const uint32_t b0 = pack_bf16(acc[db][r0 + 4] * inv, acc[db][r0 + 5] * inv);
-          const uint32_t b1 = pack_bf16(acc[db][r0 + 6] * inv, acc[db][r0 + 7] * inv);
-          const Pair x = swap_halves(a0, b0);
-          const Pair y = swap_halves(a1, b1);
-          *reinterpret_cast<u32x4*>(dst + 32 * db + 16 * hf + 8 * g) = u32x4{x.lo, y.lo, x.hi, y.hi};
-        }
-      }
-    }
+    store_tile<D, MODE>(p, acc, l_run, qrow, b, h, bh, g);
   }
 }
 
-template <int D, StoreMode MODE, bool NEG>
+// Ping-pong kernel for dense attention: 8 waves, one workgroup per CU.
+// Waves 0-3 form group 0 and waves 4-7 group 1; the SIMD that runs wave w
+// also runs wave w + 4.  A K/V stage is split into two regions separated by
+// workgroup barriers: region A (the next stage's QK^T MFMAs interleaved with
+// this stage's softmax: VALU-heavy) and region B (the PV MFMAs).  Group 1 runs
+// one region behind group 0, so that on each SIMD the softmax of one wave runs
+// beside the PV MFMAs of the other.
+//
+// Whole units (SPLIT = false) are 256-query tiles: group 0 holds queries
+// [0, 128), group 1 queries [128, 256), and both read the same K/V stages, so
+// each stage crosses the L2 -> LDS path once per 256 queries.  Group 0
+// streams K, group 1 streams V.  In barrier-separated phases t, group 0 runs
+// A(n) in t = 2n and B(n) in 2n + 1, group 1 runs A(n) in 2n + 1 and B(n) in
+// 2n + 2.  K stage j lives in kx[j % 2]; its last reader (group 1, A(j - 1))
+// ends in phase 2j - 1, and group 0 refills it with stage j + 2 in A(j).  V
+// stage j lives in vx[j % 2]; its last reader (group 1, B(j)) ends in phase
+// 2j + 2, and group 1 refills it with stage j + 2 in A(j + 1).  Each group
+// waits for its own DMA at the end of its next region B, before the barrier
+// that precedes the first reader.
+//
+// Split units (SPLIT = true) fill the last, partial round of a launch: one
+// 128-query half of a 256-query tile, with the keys split between the groups
+// (group 0 the first ceil(ns / 2) stages, group 1 the rest).  Both groups
+// hold the same queries; each streams its own K and V into its own buffers
+// with the same double-buffer schedule, and at the end group 1 hands its
+// partial (max, sum, O) to group 0 through LDS, which merges and stores.
+template <int D, StoreMode MODE, bool NEG, bool SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
+                          amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_pp_kernel(FwdParams p) {
+  constexpr int NKS = D / 16;     // QK^T contraction steps
+  constexpr int NDB = D / 32;     // 32-dim blocks of O^T
+  constexpr int NA = 2 * NKS;     // QK^T MFMAs per stage
+  constexpr int NB = 4 * NDB;     // PV MFMAs per stage
+  constexpr int KLEAD = FA_KLEAD;
+  constexpr int VLEAD = FA_VLEAD;
+  constexpr int E = Tile<D>::ELEMS;
+  constexpr int NG = SPLIT ? 2 : 1;   // K/V streams (one per group in split units)
+  // Buffer [i][e]: stream i; one object per (tensor, parity) so that the
+  // compiler can tell a DMA into one buffer from reads of another.
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[NG][E];
+  __shared__ __attribute__((aligned(16))) uint16_t kb1[NG][E];
+  __shared__ __attribute__((aligned(16))) uint16_t vb0[NG][E];
+  __shared__ __attribute__((aligned(16))) uint16_t vb1[NG][E];
+  // Group 1's running (max, sum) hand-over (split units only).
+  __shared__ float ml[SPLIT ? 2 * 256 : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wq = wave & 3;
+  const int l32 = lane & 31, g = lane >> 5;
+  const float c = p.c;
+  const float fill = NEG ? __builtin_inff() : -__builtin_inff();   // fill * c = -inf
+  const uint32_t head_bytes = (uint32_t)p.S * D * 2;
+  const int ns = (p.S + BN - 1) / BN;                               // K/V stages
+  const int nsh = (ns + 1) / 2;                                     // stages per stream (SPLIT)
+  const int nloop = SPLIT ? nsh : ns;
+  // Stage j of stream si starts at key key_of(si, j); a stage past the end is
+  // read at key S, which the buffer returns as zeros.
+  auto key_of = [&](int si, int j) {
+    const int st = si * nsh + j;
+    return st < ns ? st * BN : p.S;
+  };
+  // Stream si's K stage j sits in kbuf(si, j % 2), its V stage j in vbuf(si, j % 2).
+  auto kbuf = [&](int si, int par) -> uint16_t* { return par ? kb1[si] : kb0[si]; };
+  auto vbuf = [&](int si, int par) -> uint16_t* { return par ? vb1[si] : vb0[si]; };
+  const int own = SPLIT ? grp : 0;   // the stream this wave computes on
+
+  for (int unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
+    const int tile = SPLIT ? p.unit_base + (unit >> 1) : unit;     // 256-query tile
+    const int bh = tile / p.nqt, qt = tile - bh * p.nqt;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const size_t head_off = (size_t)bh * p.S * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_off, head_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, head_bytes);
+
+    const int qrow = SPLIT ? qt * 256 + (unit & 1) * 128 + wq * 32 + l32
+                           : qt * 256 + wave * 32 + l32;
+    bf16x8 qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, load16(rq, (uint32_t)(qrow * D * 2 + ks * 32 + g * 16)));
+
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+    float m_run = -__builtin_inff();
+    float l_run = 0.0f;
+
+    // Prologue: K stages 0 and 1 (group 0) and V stage 0 (group 1) of every
+    // stream; each wave computes the scores of its stream's first stage.
+#pragma unroll
+    for (int si = 0; si < NG; ++si) {
+      if (grp == 0) {
+        stage_dma<D, false>(kbuf(si, 0), rk, key_of(si, 0), wq, lane);
+        stage_dma<D, false>(kbuf(si, 1), rk, key_of(si, 1), wq, lane);
+      } else {
+        stage_dma<D, true>(vbuf(si, 0), rv, key_of(si, 0), wq, lane);
+      }
+    }
+    wait_dma();
+    __syncthreads();
+    f32x16 s_cur[2], s_alt[2];
+    qk_mfma<D>(s_cur, kbuf(own, 0), qf, l32, g);
+    __syncthreads();
+    if (grp == 1) __syncthreads();   // group 1 starts one region behind
+
+    // Region A of stage n (PAR = n % 2): issue this group's DMA (group 0:
+    // K stage n + 2, group 1: V stage n + 1, of every stream), then the QK^T
+    // MFMAs of stage n + 1 interleaved with the softmax of stage n.
+    auto region_a = [&](auto PAR, int n, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                        StageSoftmax<NEG, NA>& sm) {
+      constexpr int par = decltype(PAR)::value;
+#pragma unroll
+      for (int si = 0; si < NG; ++si) {
+        if (grp == 0)
+          stage_dma<D, false>(kbuf(si, par), rk, key_of(si, n + 2), wq, lane);
+        else
+          stage_dma<D, true>(vbuf(si, par ^ 1), rv, key_of(si, n + 1), wq, lane);
+      }
+      const uint16_t* const kn = kbuf(own, par ^ 1);
+      mask_tail(sc, (own * nsh + n) * BN, p.S, g, fill);
+      auto ka_read = [&](int i) { return k_operand<D>(kn, i & 1, i >> 1, l32, g); };
+      bf16x8 ka[NA];
+#pragma unroll
+      for (int i = 0; i < KLEAD; ++i) ka[i] = ka_read(i);
+      sn[0] = f32x16{};
+      sn[1] = f32x16{};
+#pragma unroll
+      for (int seg = 0; seg < NA; ++seg) {
+        if (seg + KLEAD < NA) ka[seg + KLEAD] = ka_read(seg + KLEAD);
+        sn[seg & 1] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[seg], qf[seg >> 1], sn[seg & 1], 0, 0, 0);
+        sm.piece(seg, sc, c, m_run, l_run);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // Region B of stage n: PV MFMAs over V stage n.
+    auto region_b = [&](auto PAR, const StageSoftmax<NEG, NA>& sm) {
+      constexpr int par = decltype(PAR)::value;
+      const uint16_t* const vt = vbuf(own, par);
+      auto va_read = [&](int j) { return v_operand<D>(vt, j / NDB, j % NDB, lane); };
+      bf16x8 va[NB];
+#pragma unroll
+      for (int j = 0; j < VLEAD; ++j) va[j] = va_read(j);
+      if (sm.rescale) {
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][r] *= sm.alpha;
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (j + VLEAD < NB) va[j + VLEAD] = va_read(j + VLEAD);
+        acc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], sm.p_operand(j / NDB),
+                                                               acc[j % NDB], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    for (int n = 0; n < nloop; n += 2) {
+      {
+        StageSoftmax<NEG, NA> sm;
+        region_a(std::integral_constant<int, 0>{}, n, s_cur, s_alt, sm);
+        barrier_keep_dma();
+        region_b(std::integral_constant<int, 0>{}, sm);
+        wait_dma();
+        __syncthreads();
+      }
+      if (n + 1 >= nloop) break;
+      {
+        StageSoftmax<NEG, NA> sm;
+        region_a(std::integral_constant<int, 1>{}, n + 1, s_alt, s_cur, sm);
+        barrier_keep_dma();
+        region_b(std::integral_constant<int, 1>{}, sm);
+        wait_dma();
+        __syncthreads();
+      }
+    }
+
+    // Epilogue.  Group 0's trailing region ends with the barrier that ends
+    // group 1's last PV.  In split units group 1 then hands its partial state
+    // over through the four K buffers, idle by now and written only by group
+    // 0 (whose next DMA follows its own reads): wave wq's O^T accumulator
+    // (NDB x 16 floats per lane, one buffer exactly) at float
+    // (db * 16 + r) * 64 + lane of buffer wq, its running max and sum in ml.
+    if (grp == 0) barrier_keep_dma();
+    static_assert(NDB * 16 * 64 * 4 == E * 2, "one buffer per wave");
+    float* const area = reinterpret_cast<float*>((wq & 1 ? kb1 : kb0)[(wq >> 1) & (NG - 1)]);
+    if (SPLIT && grp == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) area[(db * 16 + r) * 64 + lane] = acc[db][r];
+      ml[wq * 64 + lane] = m_run;
+      ml[256 + wq * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (SPLIT && grp == 0) {
+      const float m_y = ml[wq * 64 + lane];
+      const float l_y = ml[256 + wq * 64 + lane];
+      const float m = fmaxf(m_run, m_y);
+      const float ax = __builtin_amdgcn_exp2f(m_run - m);
+      const float ay = __builtin_amdgcn_exp2f(m_y - m);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[db][r] = acc[db][r] * ax + area[(db * 16 + r) * 64 + lane] * ay;
+      l_run = l_run * ax + l_y * ay;
+    }
+    // In split units only group 0 stores: group 1 passes its rows as S (past
+    // the end), which store_tile skips.  (A branch around the call instead
+    // makes the register allocator spill.)
+    store_tile<D, MODE>(p, acc, l_run, SPLIT && grp == 1 ? p.S : qrow, b, h, bh, g);
+  }
+}
+
+template <Variant VAR, int D, StoreMode MODE, bool NEG>
 static int launch_one(const FwdParams& p, int grid_cap, hipStream_t stream) {
   const int grid = p.units < grid_cap ? p.units : grid_cap;
-  hipLaunchKernelGGL((fa_fwd_kernel<D, MODE, NEG>), dim3(grid), dim3(kThreads), 0, stream, p);
+  if (VAR == Variant::PingPong)
+    hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, false>), dim3(grid), dim3(512), 0, stream, p);
+  else if (VAR == Variant::PingPongSplit)
+    hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, true>), dim3(grid), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fa_fwd_kernel<D, MODE, NEG>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <int D, StoreMode MODE>
+template <Variant VAR, int D, StoreMode MODE>
 static int occupancy_one(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fa_fwd_kernel<D, MODE, false>,
-                                                      kThreads, 0) == hipSuccess ? 0 : -1;
+  hipError_t e;
+  if (VAR == Variant::PingPong)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fa_fwd_pp_kernel<D, MODE, false, false>,
+                                                     512, 0);
+  else if (VAR == Variant::PingPongSplit)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fa_fwd_pp_kernel<D, MODE, false, true>,
+                                                     512, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fa_fwd_kernel<D, MODE, false>,
+                                                     kThreads, 0);
+  return e == hipSuccess ? 0 : -1;
 }
 
-int kernel_occupancy(int D, StoreMode mode, int* blocks_per_cu) {
-  if (D == 128) return mode == StoreMode::Slab ? occupancy_one<128, StoreMode::Slab>(blocks_per_cu)
-                                               : occupancy_one<128, StoreMode::Plain>(blocks_per_cu);
-  if (D == 64) return mode == StoreMode::Slab ? occupancy_one<64, StoreMode::Slab>(blocks_per_cu)
-                                              : occupancy_one<64, StoreMode::Plain>(blocks_per_cu);
-  return -1;
+template <Variant VAR, int D>
+static int occupancy_d(StoreMode mode, int* blocks) {
+  return mode == StoreMode::Slab ? occupancy_one<VAR, D, StoreMode::Slab>(blocks)
+                                 : occupancy_one<VAR, D, StoreMode::Plain>(blocks);
 }
 
-template <int D, StoreMode MODE>
+int kernel_occupancy(int D, StoreMode mode, Variant var, int* blocks_per_cu) {
+  if (D != 64 && D != 128) return -1;
+  if (var == Variant::PingPong)
+    return D == 128 ? occupancy_d<Variant::PingPong, 128>(mode, blocks_per_cu)
+                    : occupancy_d<Variant::PingPong, 64>(mode, blocks_per_cu);
+  if (var == Variant::PingPongSplit)
+    return D == 128 ? occupancy_d<Variant::PingPongSplit, 128>(mode, blocks_per_cu)
+                    : occupancy_d<Variant::PingPongSplit, 64>(mode, blocks_per_cu);
+  return D == 128 ? occupancy_d<Variant::Quad, 128>(mode, blocks_per_cu)
+                  : occupancy_d<Variant::Quad, 64>(mode, blocks_per_cu);
+}
+
+template <Variant VAR, int D, StoreMode MODE>
 static int launch_sign(const FwdParams& p, int grid_cap, hipStream_t stream) {
-  return p.c < 0.0f ? launch_one<D, MODE, true>(p, grid_cap, stream)
-                    : launch_one<D, MODE, false>(p, grid_cap, stream);
+  return p.c < 0.0f ? launch_one<VAR, D, MODE, true>(p, grid_cap, stream)
+                    : launch_one<VAR, D, MODE, false>(p, grid_cap, stream);
 }
 
-int launch_fwd(int D, StoreMode mode, const FwdParams& p, int grid_cap, hipStream_t stream) {
-  if (D == 128) return mode == StoreMode::Slab ? launch_sign<128, StoreMode::Slab>(p, grid_cap, stream)
-                                               : launch_sign<128, StoreMode::Plain>(p, grid_cap, stream);
-  if (D == 64) return mode == StoreMode::Slab ? launch_sign<64, StoreMode::Slab>(p, grid_cap, stream)
-                                              : launch_sign<64, StoreMode::Plain>(p, grid_cap, stream);
-  return -1;
+template <Variant VAR, int D>
+static int launch_d(StoreMode mode, const FwdParams& p, int grid_cap, hipStream_t stream) {
+  return mode == StoreMode::Slab ? launch_sign<VAR, D, StoreMode::Slab>(p, grid_cap, stream)
+                                 : launch_sign<VAR, D, StoreMode::Plain>(p, grid_cap, stream);
+}
+
+int launch_fwd(int D, StoreMode mode, Variant var, const FwdParams& p, int grid_cap,
+               hipStream_t stream) {
+  if (D != 64 && D != 128) return -1;
+  if (var == Variant::PingPong)
+    return D == 128 ? launch_d<Variant::PingPong, 128>(mode, p, grid_cap, stream)
+                    : launch_d<Variant::PingPong, 64>(mode, p, grid_cap, stream);
+  if (var == Variant::PingPongSplit)
+    return D == 128 ? launch_d<Variant::PingPongSplit, 128>(mode, p, grid_cap, stream)
+                    : launch_d<Variant::PingPongSplit, 64>(mode, p, grid_cap, stream);
+  return D == 128 ? launch_d<Variant::Quad, 128>(mode, p, grid_cap, stream)
+                  : launch_d<Variant::Quad, 64>(mode, p, grid_cap, stream);
 }
 
 }  // namespace fa

@@ -60,7 +60,7 @@ extern "C" {
 #define FA_EDIV (-2)          /* S is not a multiple of P */
 #define FA_EUNSUPPORTED (-3)  /* D is not 64 or 128 */
 #define FA_EALIGN (-4)        /* a tensor pointer not 16-byte aligned, mask not 8 */
-#define FA_ERANGE (-5)        /* S*D*2 bytes per head >= 2^31, or too many tiles */
+#define FA_ERANGE (-5)        /* (S+256)*D*2 bytes per head >= 2^31, or too many tiles */
 #define FA_ELAUNCH (-6)       /* the kernel launch was rejected */
 #define FA_EDEVICE (-7)       /* no usable HIP device, or device query failed */
 #define FA_EEXEC (-8)         /* (blocking entry points) execution failed */

@@ -79,6 +79,7 @@ def _plain(lib, q=A, k=B_, v=C, out=O, Bn=1, H=2, S=256, D=128, scale=0.1, mask=
     (dict(q=A + 8), -4), (dict(k=B_ + 2), -4), (dict(v=C + 4), -4), (dict(out=O + 8), -4),
     (dict(mask=M + 4), -4),
     (dict(S=(1 << 23), D=128, P=1), -5),
+    (dict(S=(1 << 23) - 256, D=128, P=1), -5),   # tile-padded offsets reach 2^31
     (dict(Bn=1 << 15, H=1 << 15, S=256, P=1), -5),
 ])
 def test_relayout_validation(lib, kw, code):

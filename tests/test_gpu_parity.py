@@ -123,6 +123,43 @@ def test_edge_shapes(B, H, S, D, P):
                         f"{(B, H, S, D, P)}")
 
 
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+# Dense launches run whole 256-query tiles, one workgroup per CU per round; a
+# last round that would fill at most half the CUs runs as half-tiles whose
+# keys are split between the two wave groups of a workgroup.  Shapes for each
+# schedule, from the CU count: (B, H, S, D, P).
+SCHEDULES = {
+    "half-tiles only, even stages": lambda n: (1, 3, 600, 128, 4),
+    "half-tiles only, odd stages": lambda n: (2, 2, 650, 64, 2),
+    "half-tiles only, two stages": lambda n: (1, 2, 100, 128, 2),
+    "whole tiles, full rounds": lambda n: (1, n, 256, 128, 2),
+    "whole tiles, partial round": lambda n: (1, (3 * n) // 4, 256, 64, 4),
+    "whole tiles + half-tiles": lambda n: (1, n + 5, 300, 128, 3),
+    "whole tiles + half-tiles, odd stages": lambda n: (2, n // 2 + 3, 520, 64, 8),
+}
+
+
+@pytest.mark.parametrize("sched", sorted(SCHEDULES))
+def test_dense_schedules(sched):
+    B, H, S, D, P = SCHEDULES[sched](_cus())
+    say(f"[sched] {sched}: B={B} H={H} S={S} D={D} P={P}")
+    q, k, v = wl.random_qkv(B, H, S, D, seed=H * 31 + S)
+    scale = 1.0 / math.sqrt(D)
+    slabs = run_slabs(to_dev(q), to_dev(k), to_dev(v), P, scale)
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    ref = oracle.relayout_split(oracle.attention(qd, kd, vd, scale), P)
+    absv = oracle.relayout_split(oracle.attention(qd, kd, np.abs(vd), scale), P)
+    assert_close(f64(slabs), ref, sched)
+    assert_within_bound(f64(slabs), ref, absv, sched)
+    t = wl.tag_inputs(B, H, S, D)
+    tags = run_slabs(to_dev(t.q), to_dev(t.k), to_dev(t.v), P, scale)
+    assert np.array_equal(tags.view(torch.int16).cpu().numpy(),
+                          oracle.relayout_index(t.v.view(torch.int16).numpy(), P))
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, -1.0 / math.sqrt(128)])
 def test_scales(scale):
     B, H, S, D, P = 1, 2, 300, 128, 3
@@ -153,12 +190,27 @@ def test_ones_v_gives_ones():
 
 # ---------------------------------------------------------------- masks
 def test_full_mask_equals_dense():
+    """A mask that keeps every tile gives the dense result.  Masked calls run
+    on the 4-wave kernel and dense ones on the 8-wave kernel (which splits the
+    keys of half-tiles), so the two sum in different orders: both must meet
+    the bound against the oracle, and the tag re-layout must be identical."""
     B, H, S, D, P = 1, 3, 1000, 128, 8
-    q, k, v = (to_dev(t) for t in wl.random_qkv(B, H, S, D, seed=14))
+    qh, kh, vh = wl.random_qkv(B, H, S, D, seed=14)
+    q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
     keep = np.ones((H, 8, 8), dtype=bool)
     a = run_slabs(q, k, v, P, 0.09, mask_to_dev(wl.pack_mask(keep)))
     b = run_slabs(q, k, v, P, 0.09)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    qd, kd, vd = qh.double().numpy(), kh.double().numpy(), vh.double().numpy()
+    ref = oracle.relayout_split(oracle.attention(qd, kd, vd, 0.09), P)
+    absv = oracle.relayout_split(oracle.attention(qd, kd, np.abs(vd), 0.09), P)
+    for got, what in ((a, "full mask"), (b, "dense")):
+        assert_close(f64(got), ref, what)
+        assert_within_bound(f64(got), ref, absv, what)
+    t = wl.tag_inputs(B, H, S, D)
+    tq, tk, tv = to_dev(t.q), to_dev(t.k), to_dev(t.v)
+    ta = run_slabs(tq, tk, tv, P, 1.0 / math.sqrt(D), mask_to_dev(wl.pack_mask(keep)))
+    tb = run_slabs(tq, tk, tv, P, 1.0 / math.sqrt(D))
+    assert torch.equal(ta.view(torch.int16), tb.view(torch.int16))
 
 
 @pytest.mark.parametrize("S,p_keep", [(1000, 0.0), (1000, 0.3), (32760 // 4, 0.3), (700, 0.7)])
