@@ -37,6 +37,16 @@ WORKLOAD_KEYS = {"video": "video-dit-share", "long": "long-video-share",
                  "image": "image-dit-share", "sparse": "block-sparse-video", "tiny": "tiny"}
 
 
+# What one fused call launches on its stream (the roofline's "launch" is that
+# call: HIP events bracket it).  Dense: the 8-wave kernel over whole 256-query
+# tiles, plus, when the last round would fill at most half of the CUs, a second
+# launch of its split-key variant for that round.  Masked: the 4-wave kernel.
+KERNEL_LABEL = {
+    True: "fa_fwd_pp_kernel<128, Slab> (whole 256-query tiles; split-key half tiles for a short last round)",
+    False: "fa_fwd_kernel<128, Slab> (4-wave, block mask)",
+}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -257,7 +267,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "fa_fwd_kernel<128, Slab>",
+                     "kernel": KERNEL_LABEL[mask is None],
                      "mean_launch_ms": round(mean_launch_ms, 4)},
         "kernel_source_sha256_16": kernel_source_hash(),
     }

@@ -63,6 +63,9 @@ constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
 #ifndef FA_WAVES_PER_EU
 #define FA_WAVES_PER_EU 2
 #endif
+#ifndef FA_MLEAD
+#define FA_MLEAD 4
+#endif
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
 
@@ -116,18 +119,28 @@ template <int D> struct Tile {
   static constexpr int TOTAL = 4 * ELEMS;            // K and V, double buffered
 };
 // K rows are read 16 at a time at one logical chunk: XOR with the row's low bits.
-template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Tile<D>::CH - 1); }
+#ifndef FA_KSWZ_MASK
+#define FA_KSWZ_MASK 15
+#endif
+template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Tile<D>::CH - 1) & FA_KSWZ_MASK; }
 // V is read by ds_read_b64_tr_b16: 4 consecutive rows at 2 consecutive chunks
 // per 16 lanes; XOR the chunk by 4 * (row % 4).
 template <int D> __device__ __forceinline__ int v_swz(int r) { return (4 * (r & 3)) & (Tile<D>::CH - 1); }
 
 // One K (SWZ_V = false) or V (true) stage of BN keys starting at key0 into
 // `buf`; keys past S come back as zeros.  Each wave issues CH/4 instructions.
+template <int D> struct Dma {
+  static constexpr int PER_WAVE4 = BN * Tile<D>::CH / (4 * 64);   // instructions per wave (4 waves)
+};
+
+// One K (SWZ_V = false) or V (true) stage of BN keys starting at key0 into
+// `buf`, shared by four waves (`wave` in [0, 4)); keys past S come back as
+// zeros.  Each wave issues Dma<D>::PER_WAVE4 instructions.
 template <int D, bool SWZ_V>
 __device__ __forceinline__ void stage_dma(uint16_t* buf, __amdgpu_buffer_rsrc_t r, int key0,
                                           int wave, int lane) {
   constexpr int CH = Tile<D>::CH;
-  constexpr int PER_WAVE = BN * CH / (4 * 64);
+  constexpr int PER_WAVE = Dma<D>::PER_WAVE4;
 #pragma unroll
   for (int q = 0; q < PER_WAVE; ++q) {
     const int blk = PER_WAVE * wave + q;           // 64-chunk block of the stage
@@ -140,8 +153,69 @@ __device__ __forceinline__ void stage_dma(uint16_t* buf, __amdgpu_buffer_rsrc_t 
   }
 }
 
+// One wave's share of a K or V stage, PW consecutive 1 KB blocks of LDS from
+// `dst` on: instruction q moves 16 bytes per lane from byte offset
+// off[q] + 1024 q of r into dst + 1024 q + 16 lane (the instruction offset
+// adds to both addresses; off[] has it taken out already).  Written as
+// inline assembly so that the compiler, which cannot see that it writes LDS,
+// does not guard later LDS reads with waits of its own: the caller waits for
+// the data (vmcnt) and synchronises the workgroup before any wave reads it.
+// M0 is named as clobbered on purpose: the instruction writes it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int PW>
+__device__ __forceinline__ void dma_stage_share(uint16_t* dst, __amdgpu_buffer_rsrc_t r,
+                                                uint32_t base, const uint32_t (&off)[PW]) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
+  static_assert(PW == 2 || PW == 4, "stage share");
+  if constexpr (PW == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds"
+        :
+        : "s"(lds), "v"(base + off[0]), "v"(base + off[1]), "v"(base + off[2]),
+          "v"(base + off[3]), "s"(r)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
+        :
+        : "s"(lds), "v"(base + off[0]), "v"(base + off[1]), "s"(r)
+        : "memory", "m0");
+  }
+}
+#pragma clang diagnostic pop
+
+// Byte offset, from the stage's first key, that lane `lane` of wave `wave`
+// (of four) reads in DMA instruction q of a K (SWZ_V = false) or V stage.
+template <int D, bool SWZ_V>
+__device__ __forceinline__ uint32_t dma_lane_off(int wave, int lane, int q) {
+  constexpr int CH = Tile<D>::CH;
+  const int blk = Dma<D>::PER_WAVE4 * wave + q;
+  const int pos = 64 * blk + lane;
+  const int row = pos / CH, pc = pos % CH;
+  const int lc = pc ^ (SWZ_V ? v_swz<D>(row) : k_swz<D>(row));
+  return (uint32_t)(row * D * 2 + lc * 16);
+}
+
 __device__ __forceinline__ void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS DMA has landed
+}
+
+// Wait until at most N of this wave's vector memory operations are in flight
+// (vmcnt(N); expcnt and lgkmcnt not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Workgroup barrier without the release/acquire fence of __syncthreads(): the
@@ -192,8 +266,9 @@ struct StageIter {
 // A operand of S^T = K Q^T: keys 32 mb + (lane % 32), dims 16 kk + 8 (lane / 32) + [0, 8).
 template <int D>
 __device__ __forceinline__ bf16x8 k_operand(const uint16_t* kbuf, int mb, int kk, int l32, int g) {
+  // Row 32 mb + l32 has the swizzle of row l32 (the swizzle masks fewer than 5 bits).
   const int r = 32 * mb + l32;
-  return *reinterpret_cast<const bf16x8*>(kbuf + r * D + 8 * ((2 * kk + g) ^ k_swz<D>(r)));
+  return *reinterpret_cast<const bf16x8*>(kbuf + r * D + 8 * ((2 * kk + g) ^ k_swz<D>(l32)));
 }
 
 // A operand of O^T = V^T P^T for 16-key step kk and 32-dim block db: lane l
@@ -204,13 +279,18 @@ __device__ __forceinline__ bf16x8 k_operand(const uint16_t* kbuf, int mb, int kk
 template <int D>
 __device__ __forceinline__ bf16x8 v_operand(const uint16_t* vbuf, int kk, int db, int lane) {
   const int j = lane & 15, grp = lane >> 4;
-  const int dim = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
+  // Rows 16 kk + 8 half + lrow; every term but lrow is a multiple of 4, so the
+  // row's swizzle is that of lrow.  The dims 32 db + 16 (grp & 1) + 4 (j & 3)
+  // sit in chunk 4 db + c0 (c0 < 4) at element 4 (j & 1); the swizzle flips
+  // only the db bits of the chunk, so each db has one per-lane offset and
+  // kk and half add constants.
+  const int lrow = 4 * (grp >> 1) + (j >> 2);
+  const int c0 = 2 * (grp & 1) + ((j & 3) >> 1);
+  const int col = 8 * ((4 * db + c0) ^ v_swz<D>(lrow)) + 4 * (j & 1);
   s16x4 h[2];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int row = 16 * kk + 8 * half + 4 * (grp >> 1) + (j >> 2);
-    h[half] = lds_read_tr(vbuf + row * D + 8 * ((dim >> 3) ^ v_swz<D>(row)) + (dim & 7));
-  }
+  for (int half = 0; half < 2; ++half)
+    h[half] = lds_read_tr(vbuf + (16 * kk + 8 * half) * D + lrow * D + col);
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
   return __builtin_bit_cast(bf16x8, v);
@@ -285,6 +365,61 @@ struct StageSoftmax {
       l_run = l_run * alpha + lsum;
       asm volatile("" ::"v"(l_run));
     }
+  }
+
+  // B operand of the PV MFMA over 16-key step kk.
+  __device__ __forceinline__ bf16x8 p_operand(int kk) const {
+    return __builtin_bit_cast(bf16x8, u32x4{pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]});
+  }
+};
+
+// Online softmax of one K/V stage as one block of VALU work (the ping-pong
+// kernel runs it in a region of its own, beside another wave's MFMAs).  The
+// same arithmetic as StageSoftmax, with independent chains for the scheduler:
+// the row extreme over four partial chains, all 32 probabilities, the row sum
+// over four partial sums (fp32 addition in a different order).
+template <bool NEG>
+struct StageProbs {
+  float alpha = 1.0f;
+  bool rescale = false;
+  uint32_t pk[16];
+
+  __device__ __forceinline__ void compute(f32x16 (&sc)[2], float c, float& m_run, float& l_run) {
+    float e[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int mb = k >> 1, r0 = 8 * (k & 1);
+      float x = sc[mb][r0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) x = NEG ? fminf(x, sc[mb][r0 + r]) : fmaxf(x, sc[mb][r0 + r]);
+      e[k] = x;
+    }
+    float ex = NEG ? fminf(fminf(e[0], e[1]), fminf(e[2], e[3]))
+                   : fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3]));
+    ex = NEG ? halves_min(ex) : halves_max(ex);
+    const float m_cand = fmaxf(m_run, ex * c);
+    rescale = __builtin_amdgcn_ballot_w64(m_cand > m_run + kTau) != 0;
+    const float m_use = rescale ? m_cand : m_run;
+    alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_use;
+    const float neg_m = -m_use;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[mb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r], c, neg_m));
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ls[r & 3] += sc[mb][r];
+#pragma unroll
+    for (int pi = 0; pi < 16; ++pi) pk[pi] = pack_bf16(sc[pi >> 3][2 * (pi & 7)], sc[pi >> 3][2 * (pi & 7) + 1]);
+    l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+    // Keep all of it in the softmax region: without these uses the compiler
+    // sinks the exponentials past the barrier into the MFMA region.
+#pragma unroll
+    for (int pi = 0; pi < 16; ++pi) asm volatile("" ::"v"(pk[pi]));
+    asm volatile("" ::"v"(l_run), "v"(alpha));
   }
 
   // B operand of the PV MFMA over 16-key step kk.
@@ -484,29 +619,36 @@ void fa_fwd_kernel(FwdParams p) {
 
 // Ping-pong kernel for dense attention: 8 waves, one workgroup per CU.
 // Waves 0-3 form group 0 and waves 4-7 group 1; the SIMD that runs wave w
-// also runs wave w + 4.  A K/V stage is split into two regions separated by
-// workgroup barriers: region A (the next stage's QK^T MFMAs interleaved with
-// this stage's softmax: VALU-heavy) and region B (the PV MFMAs).  Group 1 runs
-// one region behind group 0, so that on each SIMD the softmax of one wave runs
-// beside the PV MFMAs of the other.
+// also runs wave w + 4.  Each K/V stage n of a wave is split into two regions
+// separated by workgroup barriers: region S(n), the online softmax of the
+// stage's scores (VALU only), and region M(n), all of the stage's MFMAs (the
+// scores of stage n + 1, QK^T, and the PV product of stage n).  Group 1 runs
+// one region behind group 0, so that on every SIMD the softmax of one wave
+// issues beside the MFMAs of the other and the matrix core never waits for
+// the softmax.  Only one score tile is live per wave: M(n) writes the scores
+// that S(n + 1) consumes.
+//
+// Phases t are separated by barriers: group 0 runs S(n) in t = 2n and M(n) in
+// 2n + 1, group 1 runs S(n) in 2n + 1 and M(n) in 2n + 2.  K stage j is read in
+// M(j - 1) (phases 2j - 1 and 2j), V stage j in M(j) (phases 2j + 1 and
+// 2j + 2).  DMA is issued at the start of region S and waited for at the end
+// of the wave's next region S, before the barrier that precedes its readers.
 //
 // Whole units (SPLIT = false) are 256-query tiles: group 0 holds queries
 // [0, 128), group 1 queries [128, 256), and both read the same K/V stages, so
-// each stage crosses the L2 -> LDS path once per 256 queries.  Group 0
-// streams K, group 1 streams V.  In barrier-separated phases t, group 0 runs
-// A(n) in t = 2n and B(n) in 2n + 1, group 1 runs A(n) in 2n + 1 and B(n) in
-// 2n + 2.  K stage j lives in kx[j % 2]; its last reader (group 1, A(j - 1))
-// ends in phase 2j - 1, and group 0 refills it with stage j + 2 in A(j).  V
-// stage j lives in vx[j % 2]; its last reader (group 1, B(j)) ends in phase
-// 2j + 2, and group 1 refills it with stage j + 2 in A(j + 1).  Each group
-// waits for its own DMA at the end of its next region B, before the barrier
-// that precedes the first reader.
+// each stage crosses the L2 -> LDS path once per 256 queries.  Three buffers
+// per tensor: group 0 loads K stage n + 2 in S(n) into the slot of K stage
+// n - 1 (last read in phase 2n - 2), first read in phase 2n + 3; group 1 loads
+// V stage n + 2 in S(n) into the slot of V stage n - 1 (last read in phase
+// 2n), first read in phase 2n + 5.
 //
 // Split units (SPLIT = true) fill the last, partial round of a launch: one
 // 128-query half of a 256-query tile, with the keys split between the groups
 // (group 0 the first ceil(ns / 2) stages, group 1 the rest).  Both groups
-// hold the same queries; each streams its own K and V into its own buffers
-// with the same double-buffer schedule, and at the end group 1 hands its
+// hold the same queries and each computes on, and loads, its own K/V stream
+// with two buffers per tensor: in S(n) K stage n + 2 (into the slot of K
+// stage n, read in M(n - 1)) and V stage n + 1 (slot of V stage n - 1, read in
+// M(n - 1)), both first read in M(n + 1).  At the end group 1 hands its
 // partial (max, sum, O) to group 0 through LDS, which merges and stores.
 template <int D, StoreMode MODE, bool NEG, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
@@ -516,16 +658,19 @@ void fa_fwd_pp_kernel(FwdParams p) {
   constexpr int NDB = D / 32;     // 32-dim blocks of O^T
   constexpr int NA = 2 * NKS;     // QK^T MFMAs per stage
   constexpr int NB = 4 * NDB;     // PV MFMAs per stage
-  constexpr int KLEAD = FA_KLEAD;
-  constexpr int VLEAD = FA_VLEAD;
   constexpr int E = Tile<D>::ELEMS;
-  constexpr int NG = SPLIT ? 2 : 1;   // K/V streams (one per group in split units)
-  // Buffer [i][e]: stream i; one object per (tensor, parity) so that the
+  constexpr int NG = SPLIT ? 2 : 1;          // K/V streams
+  constexpr int NBUF = SPLIT ? 2 : 3;        // buffers per tensor and stream
+  constexpr int PW = Dma<D>::PER_WAVE4;      // DMA instructions per wave, tensor and stage
+  constexpr int NDMA = SPLIT ? 2 * PW : PW;  // DMA instructions per wave and region S
+  // Buffer [i][e] of stream i; one object per (tensor, slot) so that the
   // compiler can tell a DMA into one buffer from reads of another.
   __shared__ __attribute__((aligned(16))) uint16_t kb0[NG][E];
   __shared__ __attribute__((aligned(16))) uint16_t kb1[NG][E];
+  __shared__ __attribute__((aligned(16))) uint16_t kb2[NBUF == 3 ? NG : 1][NBUF == 3 ? E : 8];
   __shared__ __attribute__((aligned(16))) uint16_t vb0[NG][E];
   __shared__ __attribute__((aligned(16))) uint16_t vb1[NG][E];
+  __shared__ __attribute__((aligned(16))) uint16_t vb2[NBUF == 3 ? NG : 1][NBUF == 3 ? E : 8];
   // Group 1's running (max, sum) hand-over (split units only).
   __shared__ float ml[SPLIT ? 2 * 256 : 1];
 
@@ -540,16 +685,30 @@ void fa_fwd_pp_kernel(FwdParams p) {
   const int ns = (p.S + BN - 1) / BN;                               // K/V stages
   const int nsh = (ns + 1) / 2;                                     // stages per stream (SPLIT)
   const int nloop = SPLIT ? nsh : ns;
-  // Stage j of stream si starts at key key_of(si, j); a stage past the end is
-  // read at key S, which the buffer returns as zeros.
-  auto key_of = [&](int si, int j) {
-    const int st = si * nsh + j;
+  const int own = SPLIT ? grp : 0;   // the stream this wave computes on and (SPLIT) loads
+  // Stage j of this wave's stream starts at key key_of(j); a stage past the
+  // end is read at key S, which the buffer returns as zeros.
+  auto key_of = [&](int j) {
+    const int st = own * nsh + j;
     return st < ns ? st * BN : p.S;
   };
-  // Stream si's K stage j sits in kbuf(si, j % 2), its V stage j in vbuf(si, j % 2).
-  auto kbuf = [&](int si, int par) -> uint16_t* { return par ? kb1[si] : kb0[si]; };
-  auto vbuf = [&](int si, int par) -> uint16_t* { return par ? vb1[si] : vb0[si]; };
-  const int own = SPLIT ? grp : 0;   // the stream this wave computes on
+  // Stage j of the stream sits in kbuf(j % NBUF) / vbuf(j % NBUF).
+  auto kbuf = [&](int slot) -> uint16_t* {
+    if (NBUF == 3 && slot == 2) return kb2[own];
+    return slot ? kb1[own] : kb0[own];
+  };
+  auto vbuf = [&](int slot) -> uint16_t* {
+    if (NBUF == 3 && slot == 2) return vb2[own];
+    return slot ? vb1[own] : vb0[own];
+  };
+  // Per-lane offsets of this wave's share of a K and of a V stage, less the
+  // instruction offsets of dma_stage_share.
+  uint32_t koff[PW], voff[PW];
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    koff[q] = dma_lane_off<D, false>(wq, lane, q) - 1024 * q;
+    voff[q] = dma_lane_off<D, true>(wq, lane, q) - 1024 * q;
+  }
 
   for (int unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
     const int tile = SPLIT ? p.unit_base + (unit >> 1) : unit;     // 256-query tile
@@ -559,6 +718,13 @@ void fa_fwd_pp_kernel(FwdParams p) {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_off, head_bytes);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, head_bytes);
+    // This wave's share of K stage j into slot `slot`, and of V stage j.
+    auto dma_k = [&](int slot, int j) {
+      dma_stage_share<PW>(kbuf(slot) + 64 * 8 * PW * wq, rk, (uint32_t)key_of(j) * (D * 2), koff);
+    };
+    auto dma_v = [&](int slot, int j) {
+      dma_stage_share<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key_of(j) * (D * 2), voff);
+    };
 
     const int qrow = SPLIT ? qt * 256 + (unit & 1) * 128 + wq * 32 + l32
                            : qt * 256 + wave * 32 + l32;
@@ -573,106 +739,108 @@ void fa_fwd_pp_kernel(FwdParams p) {
     float m_run = -__builtin_inff();
     float l_run = 0.0f;
 
-    // Prologue: K stages 0 and 1 (group 0) and V stage 0 (group 1) of every
-    // stream; each wave computes the scores of its stream's first stage.
-#pragma unroll
-    for (int si = 0; si < NG; ++si) {
-      if (grp == 0) {
-        stage_dma<D, false>(kbuf(si, 0), rk, key_of(si, 0), wq, lane);
-        stage_dma<D, false>(kbuf(si, 1), rk, key_of(si, 1), wq, lane);
-      } else {
-        stage_dma<D, true>(vbuf(si, 0), rv, key_of(si, 0), wq, lane);
-      }
+    // Prologue: K stages 0 and 1 and V stage 0 (SPLIT: each group, its own
+    // stream) or K stages 0, 1 (group 0) and V stages 0, 1 (group 1); every
+    // wave computes the scores of its stream's first stage.
+    if (SPLIT || grp == 0) {
+      dma_k(0, 0);
+      dma_k(1, 1);
+    }
+    if (SPLIT) {
+      dma_v(0, 0);
+    } else if (grp == 1) {
+      dma_v(0, 0);
+      dma_v(1, 1);
     }
     wait_dma();
     __syncthreads();
-    f32x16 s_cur[2], s_alt[2];
-    qk_mfma<D>(s_cur, kbuf(own, 0), qf, l32, g);
+    f32x16 s[2];
+    qk_mfma<D>(s, kbuf(0), qf, l32, g);
     __syncthreads();
     if (grp == 1) __syncthreads();   // group 1 starts one region behind
 
-    // Region A of stage n (PAR = n % 2): issue this group's DMA (group 0:
-    // K stage n + 2, group 1: V stage n + 1, of every stream), then the QK^T
-    // MFMAs of stage n + 1 interleaved with the softmax of stage n.
-    auto region_a = [&](auto PAR, int n, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                        StageSoftmax<NEG, NA>& sm) {
-      constexpr int par = decltype(PAR)::value;
-#pragma unroll
-      for (int si = 0; si < NG; ++si) {
-        if (grp == 0)
-          stage_dma<D, false>(kbuf(si, par), rk, key_of(si, n + 2), wq, lane);
-        else
-          stage_dma<D, true>(vbuf(si, par ^ 1), rv, key_of(si, n + 1), wq, lane);
+    // Region S(n), SLOT = n % NBUF: this wave's DMA, the softmax of stage n,
+    // then the wait for the DMA issued in S(n - 1).
+    auto region_s = [&](auto SLOT, int n, StageProbs<NEG>& sm) {
+      constexpr int slot = decltype(SLOT)::value;
+      if (SPLIT) {
+        dma_k(slot, n + 2);                      // into the slot of K stage n
+        dma_v((slot + 1) % NBUF, n + 1);         // into the slot of V stage n - 1
+      } else if (grp == 0) {
+        dma_k((slot + 2) % NBUF, n + 2);         // into the slot of K stage n - 1
+      } else {
+        dma_v((slot + 2) % NBUF, n + 2);         // into the slot of V stage n - 1
       }
-      const uint16_t* const kn = kbuf(own, par ^ 1);
-      mask_tail(sc, (own * nsh + n) * BN, p.S, g, fill);
-      auto ka_read = [&](int i) { return k_operand<D>(kn, i & 1, i >> 1, l32, g); };
-      bf16x8 ka[NA];
-#pragma unroll
-      for (int i = 0; i < KLEAD; ++i) ka[i] = ka_read(i);
-      sn[0] = f32x16{};
-      sn[1] = f32x16{};
-#pragma unroll
-      for (int seg = 0; seg < NA; ++seg) {
-        if (seg + KLEAD < NA) ka[seg + KLEAD] = ka_read(seg + KLEAD);
-        sn[seg & 1] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[seg], qf[seg >> 1], sn[seg & 1], 0, 0, 0);
-        sm.piece(seg, sc, c, m_run, l_run);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      mask_tail(s, (own * nsh + n) * BN, p.S, g, fill);
+      sm.compute(s, c, m_run, l_run);
+      wait_vm<NDMA>();
     };
-    // Region B of stage n: PV MFMAs over V stage n.
-    auto region_b = [&](auto PAR, const StageSoftmax<NEG, NA>& sm) {
-      constexpr int par = decltype(PAR)::value;
-      const uint16_t* const vt = vbuf(own, par);
-      auto va_read = [&](int j) { return v_operand<D>(vt, j / NDB, j % NDB, lane); };
-      bf16x8 va[NB];
-#pragma unroll
-      for (int j = 0; j < VLEAD; ++j) va[j] = va_read(j);
+    // Region M(n): the scores of stage n + 1 (K stage n + 1) and PV of stage
+    // n (V stage n), interleaved: QK^T MFMA i after PV MFMA i.  After the last
+    // stage the QK^T MFMAs read a buffer of zeros and their result is unused.
+    auto region_m = [&](auto SLOT, const StageProbs<NEG>& sm) {
+      constexpr int slot = decltype(SLOT)::value;
+      const uint16_t* const kn = kbuf((slot + 1) % NBUF);
+      const uint16_t* const vt = vbuf(slot);
       if (sm.rescale) {
 #pragma unroll
         for (int i = 0; i < NDB; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][r] *= sm.alpha;
       }
+      static_assert(NA == NB, "one QK^T MFMA per PV MFMA");
+      constexpr int LEAD = FA_MLEAD;
+      auto ka_read = [&](int i) { return k_operand<D>(kn, i & 1, i >> 1, l32, g); };
+      auto va_read = [&](int j) { return v_operand<D>(vt, j / NDB, j % NDB, lane); };
+      bf16x8 ka[NA], va[NB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (j + VLEAD < NB) va[j + VLEAD] = va_read(j + VLEAD);
-        acc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], sm.p_operand(j / NDB),
-                                                               acc[j % NDB], 0, 0, 0);
+      for (int i = 0; i < LEAD; ++i) {
+        va[i] = va_read(i);
+        ka[i] = ka_read(i);
+      }
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        if (i + LEAD < NA) {
+          va[i + LEAD] = va_read(i + LEAD);
+          ka[i + LEAD] = ka_read(i + LEAD);
+        }
+        acc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], sm.p_operand(i / NDB),
+                                                               acc[i % NDB], 0, 0, 0);
+        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i >> 1],
+                                                           i < 2 ? f32x16{} : s[i & 1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
+    // One stage: S, barrier, M, barrier.
+    auto stage = [&](auto SLOT, int n) {
+      StageProbs<NEG> sm;
+      region_s(SLOT, n, sm);
+      barrier_keep_dma();
+      region_m(SLOT, sm);
+      barrier_keep_dma();
+    };
 
-    for (int n = 0; n < nloop; n += 2) {
-      {
-        StageSoftmax<NEG, NA> sm;
-        region_a(std::integral_constant<int, 0>{}, n, s_cur, s_alt, sm);
-        barrier_keep_dma();
-        region_b(std::integral_constant<int, 0>{}, sm);
-        wait_dma();
-        __syncthreads();
-      }
+    for (int n = 0; n < nloop; n += NBUF) {
+      stage(std::integral_constant<int, 0>{}, n);
       if (n + 1 >= nloop) break;
-      {
-        StageSoftmax<NEG, NA> sm;
-        region_a(std::integral_constant<int, 1>{}, n + 1, s_alt, s_cur, sm);
-        barrier_keep_dma();
-        region_b(std::integral_constant<int, 1>{}, sm);
-        wait_dma();
-        __syncthreads();
+      stage(std::integral_constant<int, 1>{}, n + 1);
+      if (NBUF == 3) {
+        if (n + 2 >= nloop) break;
+        stage(std::integral_constant<int, 2 % NBUF>{}, n + 2);
       }
     }
+    wait_dma();   // DMA of stages past the end, before the buffers are reused
 
     // Epilogue.  Group 0's trailing region ends with the barrier that ends
-    // group 1's last PV.  In split units group 1 then hands its partial state
-    // over through the four K buffers, idle by now and written only by group
-    // 0 (whose next DMA follows its own reads): wave wq's O^T accumulator
-    // (NDB x 16 floats per lane, one buffer exactly) at float
+    // group 1's last M.  In split units group 1 then hands its partial state
+    // over through stream 0's four K/V buffers, idle by now and written only
+    // by group 0 (whose next DMA follows its own reads): wave wq's O^T
+    // accumulator (NDB x 16 floats per lane, one buffer exactly) at float
     // (db * 16 + r) * 64 + lane of buffer wq, its running max and sum in ml.
     if (grp == 0) barrier_keep_dma();
     static_assert(NDB * 16 * 64 * 4 == E * 2, "one buffer per wave");
-    float* const area = reinterpret_cast<float*>((wq & 1 ? kb1 : kb0)[(wq >> 1) & (NG - 1)]);
+    float* const area = reinterpret_cast<float*>(wq == 0 ? kb0[0] : wq == 1 ? kb1[0]
+                                                 : wq == 2 ? vb0[0] : vb1[0]);
     if (SPLIT && grp == 1) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
