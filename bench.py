@@ -58,7 +58,7 @@ def kernel_source_hash() -> str:
 def load_traffic(workload: str):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"fa_fwd_slab_{workload}_counters.json")
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_pp_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:

@@ -64,7 +64,7 @@ constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
 #define FA_WAVES_PER_EU 2
 #endif
 #ifndef FA_MLEAD
-#define FA_MLEAD 4
+#define FA_MLEAD 3
 #endif
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
@@ -153,23 +153,23 @@ __device__ __forceinline__ void stage_dma(uint16_t* buf, __amdgpu_buffer_rsrc_t 
   }
 }
 
-// One wave's share of a K or V stage, PW consecutive 1 KB blocks of LDS from
-// `dst` on: instruction q moves 16 bytes per lane from byte offset
-// off[q] + 1024 q of r into dst + 1024 q + 16 lane (the instruction offset
-// adds to both addresses; off[] has it taken out already).  Written as
-// inline assembly so that the compiler, which cannot see that it writes LDS,
-// does not guard later LDS reads with waits of its own: the caller waits for
-// the data (vmcnt) and synchronises the workgroup before any wave reads it.
-// M0 is named as clobbered on purpose: the instruction writes it.
+// N consecutive 1 KB blocks of a K or V stage into LDS from `dst` on:
+// instruction i moves 16 bytes per lane from byte offset base + off[i] of r
+// into dst + 1024 i + 16 lane (the instruction offset, 1024 i, adds to both
+// addresses, so it is taken out of the global one).  Written as inline
+// assembly so that the compiler, which cannot see that it writes LDS, does
+// not guard later LDS reads with waits of its own: the caller waits for the
+// data (vmcnt) and synchronises the workgroup before any wave reads it.
+// M0 is named as clobbered on purpose: the sequence writes it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-template <int PW>
-__device__ __forceinline__ void dma_stage_share(uint16_t* dst, __amdgpu_buffer_rsrc_t r,
-                                                uint32_t base, const uint32_t (&off)[PW]) {
+template <int N>
+__device__ __forceinline__ void dma_blocks(uint16_t* dst, __amdgpu_buffer_rsrc_t r, uint32_t base,
+                                           const uint32_t* off) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
-  static_assert(PW == 2 || PW == 4, "stage share");
-  if constexpr (PW == 4) {
+  static_assert(N == 1 || N == 2 || N == 4, "block count");
+  if constexpr (N == 4) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
@@ -178,17 +178,25 @@ __device__ __forceinline__ void dma_stage_share(uint16_t* dst, __amdgpu_buffer_r
         "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
         "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds"
         :
-        : "s"(lds), "v"(base + off[0]), "v"(base + off[1]), "v"(base + off[2]),
-          "v"(base + off[3]), "s"(r)
+        : "s"(lds), "v"(base + off[0]), "v"(base - 1024 + off[1]), "v"(base - 2048 + off[2]),
+          "v"(base - 3072 + off[3]), "s"(r)
         : "memory", "m0");
-  } else {
+  } else if constexpr (N == 2) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
         "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
         "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
         :
-        : "s"(lds), "v"(base + off[0]), "v"(base + off[1]), "s"(r)
+        : "s"(lds), "v"(base + off[0]), "v"(base - 1024 + off[1]), "s"(r)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds), "v"(base + off[0]), "s"(r)
         : "memory", "m0");
   }
 }
@@ -631,8 +639,9 @@ void fa_fwd_kernel(FwdParams p) {
 // Phases t are separated by barriers: group 0 runs S(n) in t = 2n and M(n) in
 // 2n + 1, group 1 runs S(n) in 2n + 1 and M(n) in 2n + 2.  K stage j is read in
 // M(j - 1) (phases 2j - 1 and 2j), V stage j in M(j) (phases 2j + 1 and
-// 2j + 2).  DMA is issued at the start of region S and waited for at the end
-// of the wave's next region S, before the barrier that precedes its readers.
+// 2j + 2).  DMA is issued at the start of region S (split units: the K part
+// at the end of the preceding region M) and waited for at the end of the
+// wave's next region S, before the barrier that precedes its readers.
 //
 // Whole units (SPLIT = false) are 256-query tiles: group 0 holds queries
 // [0, 128), group 1 queries [128, 256), and both read the same K/V stages, so
@@ -646,9 +655,10 @@ void fa_fwd_kernel(FwdParams p) {
 // 128-query half of a 256-query tile, with the keys split between the groups
 // (group 0 the first ceil(ns / 2) stages, group 1 the rest).  Both groups
 // hold the same queries and each computes on, and loads, its own K/V stream
-// with two buffers per tensor: in S(n) K stage n + 2 (into the slot of K
-// stage n, read in M(n - 1)) and V stage n + 1 (slot of V stage n - 1, read in
-// M(n - 1)), both first read in M(n + 1).  At the end group 1 hands its
+// with two buffers per tensor: K stage n + 2 at the end of M(n - 1) (into the
+// slot of K stage n, whose last reader is that same region) and V stage n + 1
+// at the start of S(n) (slot of V stage n - 1, read in M(n - 1)), both first
+// read in M(n + 1).  At the end group 1 hands its
 // partial (max, sum, O) to group 0 through LDS, which merges and stores.
 template <int D, StoreMode MODE, bool NEG, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
@@ -701,13 +711,12 @@ void fa_fwd_pp_kernel(FwdParams p) {
     if (NBUF == 3 && slot == 2) return vb2[own];
     return slot ? vb1[own] : vb0[own];
   };
-  // Per-lane offsets of this wave's share of a K and of a V stage, less the
-  // instruction offsets of dma_stage_share.
+  // Per-lane offsets of this wave's share of a K and of a V stage.
   uint32_t koff[PW], voff[PW];
 #pragma unroll
   for (int q = 0; q < PW; ++q) {
-    koff[q] = dma_lane_off<D, false>(wq, lane, q) - 1024 * q;
-    voff[q] = dma_lane_off<D, true>(wq, lane, q) - 1024 * q;
+    koff[q] = dma_lane_off<D, false>(wq, lane, q);
+    voff[q] = dma_lane_off<D, true>(wq, lane, q);
   }
 
   for (int unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
@@ -719,11 +728,28 @@ void fa_fwd_pp_kernel(FwdParams p) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, head_bytes);
     // This wave's share of K stage j into slot `slot`, and of V stage j.
+    // This wave's share of K or V stage j into slot `slot`.
     auto dma_k = [&](int slot, int j) {
-      dma_stage_share<PW>(kbuf(slot) + 64 * 8 * PW * wq, rk, (uint32_t)key_of(j) * (D * 2), koff);
+      dma_blocks<PW>(kbuf(slot) + 64 * 8 * PW * wq, rk, (uint32_t)key_of(j) * (D * 2), koff);
     };
     auto dma_v = [&](int slot, int j) {
-      dma_stage_share<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key_of(j) * (D * 2), voff);
+      dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key_of(j) * (D * 2), voff);
+    };
+    // Part h of the DMA that region S(n) completes (SLOT = n % NBUF).  Whole
+    // units: K stage n + 2 (group 0) or V stage n + 2 (group 1) into the slot
+    // that stage n - 1 freed, all of it as part 1 at the start of S(n).
+    // Split units: K stage n + 2 into the slot of K stage n as part 0 at the
+    // end of M(n - 1) (in the prologue for n = 0), V stage n + 1 into the slot
+    // of V stage n - 1 as part 1.
+    auto stage_dma_part = [&](auto SLOT, int n, int h) {
+      constexpr int slot = decltype(SLOT)::value;
+      if (SPLIT) {
+        if (h == 0) dma_k(slot, n + 2);
+        else dma_v((slot + 1) % NBUF, n + 1);
+      } else if (h == 1) {
+        if (grp == 0) dma_k((slot + 2) % NBUF, n + 2);
+        else dma_v((slot + 2) % NBUF, n + 2);
+      }
     };
 
     const int qrow = SPLIT ? qt * 256 + (unit & 1) * 128 + wq * 32 + l32
@@ -757,20 +783,13 @@ void fa_fwd_pp_kernel(FwdParams p) {
     f32x16 s[2];
     qk_mfma<D>(s, kbuf(0), qf, l32, g);
     __syncthreads();
+    stage_dma_part(std::integral_constant<int, 0>{}, 0, 0);
     if (grp == 1) __syncthreads();   // group 1 starts one region behind
 
     // Region S(n), SLOT = n % NBUF: this wave's DMA, the softmax of stage n,
     // then the wait for the DMA issued in S(n - 1).
     auto region_s = [&](auto SLOT, int n, StageProbs<NEG>& sm) {
-      constexpr int slot = decltype(SLOT)::value;
-      if (SPLIT) {
-        dma_k(slot, n + 2);                      // into the slot of K stage n
-        dma_v((slot + 1) % NBUF, n + 1);         // into the slot of V stage n - 1
-      } else if (grp == 0) {
-        dma_k((slot + 2) % NBUF, n + 2);         // into the slot of K stage n - 1
-      } else {
-        dma_v((slot + 2) % NBUF, n + 2);         // into the slot of V stage n - 1
-      }
+      stage_dma_part(SLOT, n, 1);
       mask_tail(s, (own * nsh + n) * BN, p.S, g, fill);
       sm.compute(s, c, m_run, l_run);
       wait_vm<NDMA>();
@@ -817,6 +836,8 @@ void fa_fwd_pp_kernel(FwdParams p) {
       region_s(SLOT, n, sm);
       barrier_keep_dma();
       region_m(SLOT, sm);
+      // Part 0 of the DMA that S(n + 1) completes.
+      stage_dma_part(std::integral_constant<int, (decltype(SLOT)::value + 1) % NBUF>{}, n + 1, 0);
       barrier_keep_dma();
     };
 
