@@ -241,6 +241,31 @@ def main():
         boot.append(np.median(rng.choice(fa_, fa_.size)) / np.median(rng.choice(pa_, pa_.size)))
     ci = [float((np.percentile(boot, 2.5) - 1) * 100), float((np.percentile(boot, 97.5) - 1) * 100)]
 
+    # ---- serial baseline: plain-layout attention, then the standalone
+    # re-layout copy (the one-GPU form of attention followed by a separate
+    # exchange), same stream, K steps; and the copy alone.
+    slabs2 = torch.empty_like(slabs)
+
+    def copy():
+        fa.relayout_to_slabs_async(plain, slabs2, w.B, w.H, w.S, w.D, w.P, stream)
+
+    def timed(fn, n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(n):
+            fn()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(n)]))
+
+    for _ in range(2):
+        plain_out()
+        copy()
+    serial_ms = timed(lambda: (plain_out(), copy()), a.steps)
+    copy_ms = timed(copy, a.steps)
+    copy_bytes = 2.0 * w.B * w.H * w.S * w.D * 2
+
     achieved = flop / (mean_launch_ms * 1e-3) / 1e12
     traffic = load_traffic(a.workload)
     out = {
@@ -270,6 +295,14 @@ def main():
                      "kernel": KERNEL_LABEL[mask is None],
                      "mean_launch_ms": round(mean_launch_ms, 4)},
         "kernel_source_sha256_16": kernel_source_hash(),
+        "serial_baseline": {
+            "what": "plain-layout attention, then the standalone re-layout copy (relayout_to_slabs)",
+            "ms_per_step": round(serial_ms, 4),
+            "relayout_copy_ms": round(copy_ms, 4),
+            "relayout_copy_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+            "relayout_copy_frac_of_8TBps": round(copy_bytes / (copy_ms * 1e-3) / 8e12, 4),
+            "speedup_fused_over_serial": round(serial_ms / mean_launch_ms, 4),
+        },
     }
     if a.copy_calibration_mib:
         copy_calibration(a.copy_calibration_mib)

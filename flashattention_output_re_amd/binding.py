@@ -35,6 +35,8 @@ SIGNATURES = {
     "attn_fwd_relayout": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_fwd_plain_async": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P],
     "attn_fwd_plain": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P],
+    "relayout_to_slabs_async": [_P, _P, _I, _I, _I, _I, _I, _P],
+    "relayout_to_slabs": [_P, _P, _I, _I, _I, _I, _I],
     "attn_status_string": [_I],
     "attn_abi_version": [],
 }
@@ -157,6 +159,26 @@ def attn_fwd_plain(q, k, v, out, B, H, S, D, scale, mask=None):
     st = load_library().attn_fwd_plain(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, float(scale), _ptr(mask))
     _raise(st, "attn_fwd_plain")
+
+
+def _check_relayout(plain, out_slabs, B, H, S, D, P):
+    if P > 0 and S % P == 0:
+        _check_tensor("plain", plain, (B, H, S, D))
+        _check_tensor("out_slabs", out_slabs, (P, B, S // P, H, D))
+
+
+def relayout_to_slabs_async(plain, out_slabs, B, H, S, D, P, stream=None):
+    """Enqueue the standalone copy plain [B][H][S][D] -> slabs [P][B][S/P][H][D]."""
+    _check_relayout(plain, out_slabs, B, H, S, D, P)
+    st = load_library().relayout_to_slabs_async(_ptr(plain), _ptr(out_slabs), B, H, S, D, P,
+                                                _stream(stream))
+    _raise(st, "relayout_to_slabs_async")
+
+
+def relayout_to_slabs(plain, out_slabs, B, H, S, D, P):
+    _check_relayout(plain, out_slabs, B, H, S, D, P)
+    st = load_library().relayout_to_slabs(_ptr(plain), _ptr(out_slabs), B, H, S, D, P)
+    _raise(st, "relayout_to_slabs")
 
 
 def attention_relayout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: int,

@@ -9,6 +9,7 @@
 
 #include "../../include/fa_relayout.h"
 #include "fa_fwd_kernel.h"
+#include "fa_relayout_kernel.h"
 
 namespace {
 
@@ -122,6 +123,40 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
              ? FA_OK : FA_ELAUNCH;
 }
 
+int validate_relayout(const void* plain, const void* out, int B, int H, int S, int D, int P) {
+  if (!plain || !out) return FA_EINVAL;
+  if (B <= 0 || H <= 0 || S <= 0 || P <= 0) return FA_EINVAL;
+  if (D != 64 && D != 128) return FA_EUNSUPPORTED;
+  if (S % P != 0) return FA_EDIV;
+  if (!aligned(plain, 16) || !aligned(out, 16)) return FA_EALIGN;
+  // 32-bit chunk indices inside the kernel.
+  if ((int64_t)B * H * S * (D / 8) >= ((int64_t)1 << 31)) return FA_ERANGE;
+  return FA_OK;
+}
+
+int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return cus;
+}
+
+int run_relayout(const void* plain, void* out, int B, int H, int S, int D, int P,
+                 hipStream_t stream) {
+  const int st = validate_relayout(plain, out, B, H, S, D, P);
+  if (st != FA_OK) return st;
+  const int cus = cu_count();
+  if (cus <= 0) return FA_EDEVICE;
+  fa::RelayoutParams rp;
+  rp.B = (uint32_t)B;
+  rp.H = (uint32_t)H;
+  rp.S = (uint32_t)S;
+  rp.Sp = (uint32_t)(S / P);
+  rp.rows = (uint32_t)B * (uint32_t)H * (uint32_t)S;
+  const int grid = fa::relayout_grid(D, rp.rows, cus);
+  return fa::launch_relayout(D, plain, out, rp, grid, stream) == 0 ? FA_OK : FA_ELAUNCH;
+}
+
 int finish_blocking(int st) {
   if (st != FA_OK) return st;
   return hipStreamSynchronize(nullptr) == hipSuccess ? FA_OK : FA_EEXEC;
@@ -154,6 +189,15 @@ int attn_fwd_plain(const void* q, const void* k, const void* v, void* out, int B
                    int D, float scale, const uint64_t* mask) {
   return finish_blocking(
       run(fa::StoreMode::Plain, q, k, v, out, B, H, S, D, 1, scale, mask, nullptr));
+}
+
+int relayout_to_slabs_async(const void* plain, void* out_slabs, int B, int H, int S, int D,
+                            int P, void* stream) {
+  return run_relayout(plain, out_slabs, B, H, S, D, P, static_cast<hipStream_t>(stream));
+}
+
+int relayout_to_slabs(const void* plain, void* out_slabs, int B, int H, int S, int D, int P) {
+  return finish_blocking(run_relayout(plain, out_slabs, B, H, S, D, P, nullptr));
 }
 
 const char* attn_status_string(int status) {

@@ -5,7 +5,7 @@
  * What it computes.  One GPU's share of Ulysses sequence-parallel attention
  * in diffusion-transformer inference (X-Stage abstract, CatalyzeX and fugumt
  * pages): for its H local heads over the whole sequence of S tokens, each
- * 128-query output tile runs a non-causal FlashAttention forward pass (online
+ * output tile of queries runs a non-causal FlashAttention forward pass (online
  * softmax over K/V tiles), and its owner stores the finished tile straight
  * into the sequence-sharded layout before resuming the next tile's Q-loop,
  * with no separate communication wavefront ("Technical Summary: X-Stage in
@@ -89,6 +89,22 @@ int attn_fwd_plain_async(const void* q, const void* k, const void* v, void* out,
 
 int attn_fwd_plain(const void* q, const void* k, const void* v, void* out,
                    int B, int H, int S, int D, float scale, const uint64_t* mask);
+
+/* Standalone head-to-sequence re-layout: out_slabs[p][b][t][h][d] =
+ * plain[b][h][p*(S/P) + t][d], a bit-exact copy of bf16 (or any 16-bit)
+ * elements.  With attn_fwd_plain it forms the serial baseline the fused
+ * kernel is measured against: attention first, then a separate exchange of
+ * its output ("Technical Summary: X-Stage in DiT Inference", Results, the
+ * serial FlashAttention-then-All-to-All execution the speedups are quoted
+ * over; on one GPU the exchange is this local copy into P slabs).
+ * plain: [B][H][S][D]; out_slabs: [P][B][S/P][H][D]; both contiguous, 16-byte
+ * aligned, not overlapping.  Same validation and status codes as
+ * attn_fwd_relayout (D must be 64 or 128; FA_ERANGE when B*H*S*D/8 >= 2^31).
+ * HBM-bound: reads and writes B*H*S*D*2 bytes each. */
+int relayout_to_slabs_async(const void* plain, void* out_slabs, int B, int H, int S, int D,
+                            int P, void* stream);
+
+int relayout_to_slabs(const void* plain, void* out_slabs, int B, int H, int S, int D, int P);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* attn_status_string(int status);

@@ -25,7 +25,8 @@ def _header():
 
 def declared_functions():
     text = re.sub(r"/\*.*?\*/", "", _header(), flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:attn|relayout)_\w+)\s*\(",
+                                 text, re.M)))
 
 
 def declared_status_codes():
@@ -94,16 +95,33 @@ def test_plain_validation(lib, kw, code):
     assert _plain(lib, **kw) == code
 
 
+def _copy(lib, plain=A, out=O, Bn=1, H=2, S=256, D=128, P=2):
+    return lib.relayout_to_slabs_async(plain, out, Bn, H, S, D, P, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(plain=None), -1), (dict(out=None), -1), (dict(Bn=0), -1), (dict(H=-2), -1),
+    (dict(S=0), -1), (dict(P=0), -1), (dict(D=96), -3), (dict(D=0), -3),
+    (dict(S=255, P=2), -2), (dict(plain=A + 8), -4), (dict(out=O + 4), -4),
+    (dict(Bn=1 << 10, H=1 << 10, S=1 << 10, D=128, P=1), -5),
+])
+def test_relayout_copy_validation(lib, kw, code):
+    assert _copy(lib, **kw) == code
+
+
 def test_blocking_entry_points_validate(lib):
     assert lib.attn_fwd_relayout(None, B_, C, O, 1, 1, 256, 128, 2, 0.1, None) == -1
     assert lib.attn_fwd_relayout(A, B_, C, O, 1, 1, 256, 128, 3, 0.1, None) == -2
     assert lib.attn_fwd_plain(A, B_, C, O, 1, 1, 256, 48, 0.1, None) == -3
+    assert lib.relayout_to_slabs(None, O, 1, 1, 256, 128, 2) == -1
+    assert lib.relayout_to_slabs(A, O, 1, 1, 256, 128, 3) == -2
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
 def test_valid_arguments_without_device_report_no_device(lib):
     assert _relayout(lib) == -7
     assert _plain(lib) == -7
+    assert _copy(lib) == -7
 
 
 def test_python_binding_raises(lib):
