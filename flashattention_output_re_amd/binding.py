@@ -37,6 +37,7 @@ SIGNATURES = {
     "attn_fwd_plain": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P],
     "relayout_to_slabs_async": [_P, _P, _I, _I, _I, _I, _I, _P],
     "relayout_to_slabs": [_P, _P, _I, _I, _I, _I, _I],
+    "burst_gap_run_async": [_P, _P, _I, _I, _I, _I, _I, _P],
     "attn_status_string": [_I],
     "attn_abi_version": [],
 }

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libfa_relayout.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["fa_abi.hip", "fa_fwd_kernel.hip", "fa_relayout_kernel.hip"]
+SOURCES = ["fa_abi.hip", "fa_fwd_kernel.hip", "fa_relayout_kernel.hip", "burst_gap.hip"]
 ARCH = "gfx950"
 
 # hipcc must not emit packed fp32 VALU ops (v_pk_fma_f32 and friends).  The

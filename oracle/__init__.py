@@ -25,8 +25,13 @@ FlashAttention; "Technical Summary: X-Stage in DiT Inference", Key
 Contributions 3 (FlashAttention-A2A piggybacking) says the output-tile owner
 stores the tile to its destination and resumes the next tile's Q-loop.  The
 ScalingAttention abstract (CatalyzeX page) describes the bit-wise block-sparse
-kernel.  The pages print no formula, layout or worked example; every reading
-taken where they are silent is listed with the design notes.
+kernel.  For attention and the re-layout the pages print no formula, layout
+or worked example; every reading taken where they are silent is listed with
+the design notes.
+
+* ``burst_gap`` -- the one formula the pages do print: the Burst-Gap model of
+  sender-visible store-issue time (Methodology section of the technical
+  summary), used to check the fit of the store-burst microbenchmark.
 
 Pins (tests/test_oracle_pins.py): hand-derived exact examples
 (tests/golden/), identical keys -> mean of V, one dominant score -> that V
@@ -37,6 +42,7 @@ and planted mistakes that the pins must catch.  Every function here is pinned.
 """
 from .attn import attention, attention_probs, unpack_mask
 from .relayout import relayout_split, relayout_index, plain_layout
+from . import burst_gap
 
 __all__ = ["attention", "attention_probs", "unpack_mask",
-           "relayout_split", "relayout_index", "plain_layout"]
+           "relayout_split", "relayout_index", "plain_layout", "burst_gap"]
