@@ -41,7 +41,11 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == set(binding.SIGNATURES), names
+    other = os.path.join(ROOT, "include", "fa_burst_gap.h")   # the microbenchmark's header
+    with open(other) as f:
+        extra = re.findall(r"^\s*int\s+(\w+)\s*\(", re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S),
+                           re.M)
+    assert set(names) | set(extra) == set(binding.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n), n
 
