@@ -163,7 +163,7 @@ def predict_fused(fitres, tile_bytes=256 * 128 * 2, producers=256, tile_compute_
 def default_configs(quick: bool):
     ks = [256] if quick else [64, 256]
     vps = [64 << 10, 256 << 10] if quick else [16 << 10, 64 << 10, 256 << 10, 1 << 20]
-    gaps = [0, 300, 3000, 30000] if quick else [0, 100, 300, 1000, 3000, 10000, 30000]
+    gaps = [0, 300, 3000, 30000] if quick else [0, 10, 30, 60, 100, 300, 1000, 3000, 10000, 30000]
     nts = [False] if quick else [False, True]
     return [(k, vp, g, nt) for nt in nts for k in ks for vp in vps for g in gaps]
 
