@@ -1,36 +1,38 @@
 // Fused FlashAttention forward + Ulysses slab store for gfx950 (MI355X).
 //
-// Persistent workgroups of 4 wavefronts (two per CU) own 128-query output tiles
-// of one (batch, head) at a time: it streams the K/V tiles of the whole
-// sequence through LDS, runs QK^T and PV on the bf16 MFMA units with an fp32
-// online softmax, and in the epilogue stores the finished tile straight into
-// the P destination slabs of the head-to-sequence re-layout, then moves on to
-// its next output tile without waiting for those stores ("Technical Summary:
-// X-Stage in DiT Inference", Key Contributions 3: the output-tile owner issues
-// the stores and resumes the next tile's Q-loop; no dedicated communication
-// wavefront).  StoreMode::Plain runs the same body but writes [B][H][S][D].
+// Persistent workgroups own output tiles of one (batch, head) at a time: they
+// stream the K/V tiles of the whole sequence through LDS, run QK^T and PV on
+// the bf16 MFMA units with an fp32 online softmax, and in the epilogue store
+// the finished tile straight into the P destination slabs of the
+// head-to-sequence re-layout, then move on to the next output tile without
+// waiting for those stores ("Technical Summary: X-Stage in DiT Inference",
+// Key Contributions 3: the output-tile owner issues the stores and resumes
+// the next tile's Q-loop; no dedicated communication wavefront).
+// StoreMode::Plain runs the same body but writes [B][H][S][D].
 //
-// Layout choices (per wavefront, 32 queries):
+// Two kernels:
+//   fa_fwd_pp_kernel (dense): 8 waves, one workgroup per CU, 256-query tiles,
+//   softmax and MFMA work in separate regions run by two wave groups in
+//   alternation (its own header comment below has the schedule).
+//   fa_fwd_kernel (block mask): 4 waves, two workgroups per CU, 128-query
+//   tiles (one mask row), the next stage's QK^T MFMAs interleaved with the
+//   current stage's softmax inside each wave.
+//
+// Layout choices (per wavefront, 32 queries), shared by both:
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims of K from
 //   LDS, B = 16 dims x 32 queries of Q held in VGPRs.  The accumulator puts one
 //   query per lane (lane % 32) and 16 keys per lane, so a row's max and sum are
 //   lane-local apart from one exchange between the wave halves
 //   (v_permlane32_swap).
 //   O^T = V^T P^T: the S^T accumulator, rounded to bf16, is directly the B
-//   operand (same query per lane, keys as the contraction index).  V is
-//   written to LDS as V^T with the keys of each 16-key group permuted so that
-//   one ds_read_b128 yields exactly the 8 keys a half-wave contributes.
+//   operand (same query per lane, keys as the contraction index).  V stays
+//   row-major in LDS; the A operand comes from two ds_read_b64_tr_b16 per MFMA
+//   whose row addresses put the keys in the accumulator's order.
 //   The O^T accumulator again holds one query per lane; one permlane32 swap
 //   turns its 4-wide runs of d into 8 consecutive d, so the epilogue issues
 //   128-bit stores.
-//
-// Schedule.  On gfx950 a wavefront overlaps an MFMA with the independent VALU
-// work issued after it, so each K/V stage is software-pipelined inside the
-// wave: the QK^T MFMAs of the next stage are interleaved with the softmax of
-// the current one, and the PV MFMAs of the current stage follow.  K/V tiles
-// reach LDS by DMA, so the 256 VGPRs of two waves per SIMD (two workgroups
-// per CU) hold both score tiles, the Q fragments and the O accumulator; the
-// second wave on each SIMD covers the first one's LDS and barrier waits.
+//   K/V stages reach LDS by buffer_load ... lds DMA with XOR-swizzled 16-byte
+//   chunks (conflict-free operand reads).
 //
 // Softmax runs in the log2 domain (c = scale * log2 e, p = exp2(s c - m)).
 // The running max is only raised when some row of the wave exceeds it by more
@@ -799,6 +801,10 @@ void fa_fwd_pp_kernel(FwdParams p) {
     // stage the QK^T MFMAs read a buffer of zeros and their result is unused.
     auto region_m = [&](auto SLOT, const StageProbs<NEG>& sm) {
       constexpr int slot = decltype(SLOT)::value;
+      // Raised wave priority while this wave issues MFMAs: when both waves
+      // of a SIMD have an instruction ready, the matrix core's feeder goes
+      // first and the softmax wave's VALU work fills the gaps.
+      __builtin_amdgcn_s_setprio(2);
       const uint16_t* const kn = kbuf((slot + 1) % NBUF);
       const uint16_t* const vt = vbuf(slot);
       if (sm.rescale) {
@@ -829,6 +835,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
                                                            i < 2 ? f32x16{} : s[i & 1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     // One stage: S, barrier, M, barrier.
     auto stage = [&](auto SLOT, int n) {
