@@ -56,6 +56,9 @@ constexpr int kThreads = 256;
 constexpr int BM = 128;          // queries per output tile (= mask tile)
 constexpr int BN = 64;           // keys per LDS stage
 constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
+// Tuning knobs, overridable at build time (-D): operand reads issued ahead of
+// their MFMA in the 4-wave kernel (K, V) and in the ping-pong kernel's MFMA
+// region, and waves per SIMD of the 4-wave kernel.
 #ifndef FA_KLEAD
 #define FA_KLEAD 3
 #endif
@@ -121,10 +124,7 @@ template <int D> struct Tile {
   static constexpr int TOTAL = 4 * ELEMS;            // K and V, double buffered
 };
 // K rows are read 16 at a time at one logical chunk: XOR with the row's low bits.
-#ifndef FA_KSWZ_MASK
-#define FA_KSWZ_MASK 15
-#endif
-template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Tile<D>::CH - 1) & FA_KSWZ_MASK; }
+template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Tile<D>::CH - 1); }
 // V is read by ds_read_b64_tr_b16: 4 consecutive rows at 2 consecutive chunks
 // per 16 lanes; XOR the chunk by 4 * (row % 4).
 template <int D> __device__ __forceinline__ int v_swz(int r) { return (4 * (r & 3)) & (Tile<D>::CH - 1); }

@@ -122,9 +122,10 @@ def slab_rows(slabs: torch.Tensor, rows, S: int, P: int) -> np.ndarray:
 def sample_rows(S: int, P: int, seed: int = 0, n_random: int = 24) -> np.ndarray:
     """Rows at tile edges, slab edges, the ragged tail and some random ones."""
     Sp = S // P
-    cand = {0, 1, 31, 32, 63, 64, 127, 128, 129, S - 1, S - 2, S - 33}
-    last = ((S - 1) // 128) * 128
-    cand |= {last, last - 1, last + 1}
+    cand = {0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, 257, 383, 384, S - 1, S - 2, S - 33}
+    for tile in (128, 256):        # the last tile of each tiling, and its halves
+        last = ((S - 1) // tile) * tile
+        cand |= {last, last - 1, last + 1, last + tile // 2 - 1, last + tile // 2}
     for p in range(1, P):
         cand |= {p * Sp - 1, p * Sp, p * Sp + 1}
     r = np.random.default_rng(seed)

@@ -213,17 +213,21 @@ def test_full_mask_equals_dense():
     assert torch.equal(ta.view(torch.int16), tb.view(torch.int16))
 
 
-@pytest.mark.parametrize("S,p_keep", [(1000, 0.0), (1000, 0.3), (32760 // 4, 0.3), (700, 0.7)])
-def test_masked_parity(S, p_keep):
-    B, H, D, P = 1, 3, 128, 4 if S % 4 == 0 else 1
+@pytest.mark.parametrize("S,p_keep,B,D,scale", [
+    (1000, 0.0, 1, 128, 0.088), (1000, 0.3, 1, 128, 0.088), (32760 // 4, 0.3, 1, 128, 0.088),
+    (700, 0.7, 1, 128, 0.088), (1000, 0.5, 2, 64, 0.125), (777, 0.4, 3, 128, -0.09),
+    (129, 0.5, 2, 64, 0.2),
+])
+def test_masked_parity(S, p_keep, B, D, scale):
+    H, P = 3, 4 if S % 4 == 0 else 1
     q, k, v = wl.random_qkv(B, H, S, D, seed=S + 1)
     keep = wl.tile_mask_bool(H, S, p_keep, seed=S)
     words = wl.pack_mask(keep)
-    slabs = run_slabs(to_dev(q), to_dev(k), to_dev(v), P, 0.088, mask_to_dev(words))
+    slabs = run_slabs(to_dev(q), to_dev(k), to_dev(v), P, scale, mask_to_dev(words))
     rows = None if S <= 1000 else sample_rows(S, P, seed=S)
     qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
-    ref = oracle.attention(qd, kd, vd, 0.088, words, rows=rows)
-    absv = oracle.attention(qd, kd, np.abs(vd), 0.088, words, rows=rows)
+    ref = oracle.attention(qd, kd, vd, scale, words, rows=rows)
+    absv = oracle.attention(qd, kd, np.abs(vd), scale, words, rows=rows)
     if rows is None:
         got, ref, absv = f64(slabs), oracle.relayout_split(ref, P), oracle.relayout_split(absv, P)
     else:
