@@ -244,6 +244,15 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
+// XCD-aware order of a persistent grid of G workgroups.  Workgroups are dealt
+// to the 8 XCDs round-robin by id, so with this slot number XCD x takes, in
+// each round of G units, the G / 8 consecutive units from x * G / 8 on (tiles
+// of one head, whose K/V stream its L2 then fetches once) rather than every
+// 8th unit.  A bijection on [0, G); the identity when G is not a multiple of 8.
+__device__ __forceinline__ int xcd_slot(int block, int G) {
+  return (G % 8 == 0) ? (block % 8) * (G / 8) + block / 8 : block;
+}
+
 // Iterates the K/V stages (BN keys each) a query tile attends to: all stages
 // for dense attention, or the stages of the kept 128-key mask tiles.
 struct StageIter {
@@ -506,7 +515,9 @@ void fa_fwd_kernel(FwdParams p) {
   const float fill = NEG ? __builtin_inff() : -__builtin_inff();   // fill * c = -inf
   const uint32_t head_bytes = (uint32_t)p.S * D * 2;
 
-  for (int unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
+  const int slot_id = xcd_slot(blockIdx.x, gridDim.x);
+  for (int base = 0; base + slot_id < p.units; base += gridDim.x) {
+    const int unit = base + slot_id;
     const int bh = unit / p.nqt, qt = unit - bh * p.nqt;
     const int b = bh / p.H, h = bh - b * p.H;
     const size_t head_off = (size_t)bh * p.S * D;
@@ -721,7 +732,9 @@ void fa_fwd_pp_kernel(FwdParams p) {
     voff[q] = dma_lane_off<D, true>(wq, lane, q);
   }
 
-  for (int unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
+  const int slot_id = xcd_slot(blockIdx.x, gridDim.x);
+  for (int base = 0; base + slot_id < p.units; base += gridDim.x) {
+    const int unit = base + slot_id;
     const int tile = SPLIT ? p.unit_base + (unit >> 1) : unit;     // 256-query tile
     const int bh = tile / p.nqt, qt = tile - bh * p.nqt;
     const int b = bh / p.H, h = bh - b * p.H;
