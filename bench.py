@@ -30,6 +30,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+PEAK_SCLK_MHZ = 2400.0        # the clock that peak is quoted at
+EXP_PER_CLK = 256 * 4 * 4     # v_exp_f32 results per clock, whole chip
+LDS_B_PER_CLK_CU = 260.0      # measured LDS read rate per CU
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_output_re_amd/csrc/fa_fwd_kernel.hip",
                   "flashattention_output_re_amd/csrc/fa_fwd_kernel.h"]
@@ -106,6 +109,107 @@ def cpu_baseline(name: str, target_s: float):
             "sample": f"{name}: {blocks} blocks of 128 query rows ({done_rows} rows, heads "
                       f"{min(heads)}-{max(heads)}) against all {w.S} keys, float64 numpy, "
                       f"{el:.1f} s"}
+
+
+class ClockSampler:
+    """Shader clock of the GPU torch uses while it runs the fused kernel, read
+    through amdsmi (per-XCD current GFX clocks, averaged).  The driver refreshes
+    these metrics only every few hundred milliseconds, so `window()` keeps the
+    GPU busy with back-to-back calls for about `seconds` and keeps the samples
+    from its second half.  Reports nothing if amdsmi cannot see the device."""
+
+    def __init__(self):
+        self.handle, self.error, self.samples = None, None, []
+        try:
+            import amdsmi
+            import torch
+            self._amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
+                if int(bdf.split(":")[1], 16) == bus:
+                    self.handle = h
+            if self.handle is None:
+                self.error = f"no amdsmi device on PCI bus {bus:#x}"
+        except Exception as e:  # noqa: BLE001 - the clock is reported, not required
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        xcd = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+        if xcd:
+            return sum(xcd) / len(xcd)
+        c = m.get("current_gfxclk")
+        return float(c) if isinstance(c, (int, float)) and c > 0 else None
+
+    def window(self, call, launch_s: float, seconds: float = 1.5, max_calls: int = 30000):
+        import threading
+        import torch
+        if self.handle is None:
+            return
+        n = max(1, min(max_calls, int(seconds / max(launch_s, 1e-6))))
+        stop = threading.Event()
+        t_start = time.perf_counter()
+        span = n * launch_s
+
+        def run():
+            while not stop.is_set():
+                try:
+                    c = self._read()
+                except Exception as e:  # noqa: BLE001
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                if c is not None and time.perf_counter() - t_start > 0.5 * span:
+                    self.samples.append(c)
+                stop.wait(0.02)
+
+        for _ in range(n):
+            call()
+        th = threading.Thread(target=run, daemon=True)
+        th.start()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        try:
+            self._amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+
+    def summary(self, achieved_tflops: float):
+        import numpy as np
+        if not self.samples:
+            return {"sclk_mhz": None, "samples": 0, "error": self.error}
+        mhz = float(np.median(self.samples))
+        adj = PEAK_TFLOPS * mhz / PEAK_SCLK_MHZ
+        return {"sclk_mhz": round(mhz, 1),
+                "sclk_mhz_min_max": [round(min(self.samples), 1), round(max(self.samples), 1)],
+                "samples": len(self.samples),
+                "source": "amdsmi per-XCD current GFX clock, mean over XCDs, sampled over the "
+                          "second half of a ~1.5 s run of back-to-back fused calls",
+                "clock_adjusted_peak_tflops": round(adj, 1),
+                "frac_of_clock_adjusted_peak": round(achieved_tflops / adj, 4)}
+
+
+def secondary_bounds(flop: float, D: int, launch_s: float, sclk_mhz):
+    """Rates of the two other resources the kernel leans on, per fused call.
+    exp2: one per score, B*H*S^2 dense (flop / (4 D) in general), against the
+    transcendental unit's rate of 4 results per clock per SIMD (a wave's
+    v_exp_f32 occupies it 16 clocks): 256 CUs x 4 SIMDs x 4 = 4096 per clock.
+    LDS: every 32x32x16 MFMA (32768 FLOP) reads one 1 KiB operand from LDS
+    (K for QK^T, V through the transposing read for PV), flop / 32 bytes,
+    against ~260 B per clock per CU, the rate an in-bounds probe sustained."""
+    n_exp = flop / (4.0 * D)
+    lds = flop / 32.0
+    out = {"exp2_count": n_exp, "exp2_per_s": round(n_exp / launch_s, 1),
+           "exp2_frac_of_peak_2400MHz": round(n_exp / launch_s / (EXP_PER_CLK * 2.4e9), 4),
+           "lds_read_bytes": lds, "lds_read_TBps": round(lds / launch_s / 1e12, 2),
+           "lds_frac_of_measured_2400MHz": round(lds / launch_s / (LDS_B_PER_CLK_CU * 256 * 2.4e9), 4)}
+    if sclk_mhz:
+        f = sclk_mhz * 1e6
+        out["exp2_frac_at_sclk"] = round(n_exp / launch_s / (EXP_PER_CLK * f), 4)
+        out["lds_frac_at_sclk"] = round(lds / launch_s / (LDS_B_PER_CLK_CU * 256 * f), 4)
+    return out
 
 
 def copy_calibration(mib: int):
@@ -268,6 +372,9 @@ def main():
 
     achieved = flop / (mean_launch_ms * 1e-3) / 1e12
     traffic = load_traffic(a.workload)
+    clock = ClockSampler()
+    clock.window(fused, mean_launch_ms * 1e-3)
+    clk = clock.summary(achieved)
     out = {
         "metric": "fused attn+relayout TFLOP/s at 1 GPU; % bf16 MFMA peak; fused-store overhead %",
         "value": round(tflops, 2),
@@ -293,7 +400,11 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": traffic,
                      "kernel": KERNEL_LABEL[mask is None],
-                     "mean_launch_ms": round(mean_launch_ms, 4)},
+                     "mean_launch_ms": round(mean_launch_ms, 4),
+                     "launch_ms_p10_p50_p90": [round(float(np.percentile(launch_ms, x)), 4)
+                                               for x in (10, 50, 90)]},
+        "clock": clk,
+        "secondary_bounds": secondary_bounds(flop, w.D, mean_launch_ms * 1e-3, clk.get("sclk_mhz")),
         "kernel_source_sha256_16": kernel_source_hash(),
         "serial_baseline": {
             "what": "plain-layout attention, then the standalone re-layout copy (relayout_to_slabs)",
