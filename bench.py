@@ -58,10 +58,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def profile_prefix(workload: str) -> str:
+    """File-name stem of a workload's rocprofv3 summaries under profiles/: the
+    kernel family that runs it, then the workload."""
+    import workloads as wl
+    fam = "fa_fwd_quad" if wl.WORKLOADS[workload].keep_prob is not None else "fa_fwd_pp"
+    return f"{fam}_{workload}"
+
+
 def load_traffic(workload: str):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"fa_fwd_pp_{workload}_counters.json")
+    path = os.path.join(ROOT, "profiles", f"{profile_prefix(workload)}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -254,6 +262,161 @@ def summarize(kind: str, path: str):
             print(f"| {kname} | {cname} | {len(d)} | {statistics.mean(d.values()):.6g} |")
 
 
+def _counter_means(path: str) -> dict:
+    """{(kernel, counter): mean over dispatches} from rocprofv3 --pmc CSV output."""
+    import csv
+    import glob
+    import statistics
+    per = {}
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: statistics.mean(v.values()) for k, v in per.items()}
+
+
+def write_profile_report(workload: str, d: str):
+    """Write profiles/<kernel>_<workload>_{kernel_trace.md,counters.md,counters.json}
+    from the rocprofv3 output directories that the commands printed in them
+    leave under `d` (trace_<w>, pmc_{FETCH_SIZE,WRITE_SIZE,sq1,sq2}_<w>) and the
+    bench.py JSON line in d/bench_<w>.json."""
+    import contextlib
+    import csv
+    import glob
+    import io
+    import numpy as np
+    import workloads as wl
+    w = wl.WORKLOADS[workload]
+    keep = wl.tile_mask_bool(w.H, w.S, w.keep_prob, w.seed) if w.keep_prob is not None else None
+    flop = wl.flop_count(w.B, w.H, w.S, w.D, keep)
+    stem = os.path.join(ROOT, "profiles", profile_prefix(workload))
+    short = (f"python bench.py --workload {workload} --steps 10 --warmup 2 --overhead-pairs 4 "
+             "--no-cpu-baseline --no-clock")
+    sq1 = ("SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
+           "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_MISC")
+    sq2 = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS "
+           "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE")
+
+    def summary(kind, sub):
+        buf = io.StringIO()
+        with contextlib.redirect_stdout(buf):
+            summarize(kind, os.path.join(d, sub))
+        return buf.getvalue()
+
+    def fused_only(text):
+        return "\n".join(l for l in text.splitlines()
+                         if "(fa::StoreMode)1" not in l and "relayout_kernel" not in l
+                         and "elementwise" not in l and "copyBuffer" not in l
+                         and "fillBuffer" not in l)
+
+    stats_f = glob.glob(os.path.join(d, f"trace_{workload}", "**", "*kernel_stats.csv"), recursive=True)[0]
+    stats = {r["Name"]: r for r in csv.DictReader(open(stats_f))}
+    fused = sorted(n for n in stats if "fa_fwd" in n and "(fa::StoreMode)0" in n)
+    avg_s = {n: float(stats[n]["AverageNs"]) * 1e-9 for n in fused}
+    call_s = sum(avg_s.values())
+    bj = json.loads(open(os.path.join(d, f"bench_{workload}.json")).read().strip().splitlines()[-1])
+    fe, wr = _counter_means(os.path.join(d, f"pmc_FETCH_SIZE_{workload}")), \
+        _counter_means(os.path.join(d, f"pmc_WRITE_SIZE_{workload}"))
+    c1, c2 = _counter_means(os.path.join(d, f"pmc_sq1_{workload}")), \
+        _counter_means(os.path.join(d, f"pmc_sq2_{workload}"))
+    copy = next(k for (k, c) in fe if "copyBuffer" in k)
+    fscale = 1024.0 * 1024 / fe[(copy, "FETCH_SIZE")]        # the 1 GiB copy reads 1 GiB
+    wscale = 1024.0 * 1024 / wr[(copy, "WRITE_SIZE")]
+    fetch_b = {n: fe[(n, "FETCH_SIZE")] * 1024 * fscale for n in fused}
+    write_b = {n: wr[(n, "WRITE_SIZE")] * 1024 * wscale for n in fused}
+    bytes_call = sum(fetch_b.values()) + sum(write_b.values())
+    min_bytes = 4.0 * w.B * w.H * w.S * w.D * 2
+    hsh = kernel_source_hash()
+    title = {"video": "Video-DiT share", "long": "long video share", "image": "Image-DiT share",
+             "sparse": "block-sparse video", "tiny": "tiny case"}[workload]
+    shape = f"B={w.B}, H={w.H}, S={w.S}, D={w.D}, P={w.P}" + (
+        f", {100 * float(keep.mean()):.1f}% of 128x128 tiles kept" if keep is not None else "")
+
+    tr = [f"# Fused kernel on the {title} ({shape}): kernel trace\n",
+          "Command (from the repository root, after `python -m flashattention_output_re_amd.build`):\n",
+          "```",
+          f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_{workload} -o run -- {short}",
+          f"python bench.py --summarize trace {d}/trace_{workload}",
+          "```\n",
+          f"Kernel source sha256/16: {hsh}. StoreMode 0 = slab (fused re-layout), 1 = plain "
+          "[B][H][S][D] (the overhead twin and the serial baseline's attention). For fa_fwd_pp_kernel "
+          "the last template flag is false for whole 256-query tiles and true for split-key half tiles "
+          "(a short last round, second launch on the same stream); fa_fwd_kernel is the 4-wave kernel "
+          "that runs masked calls. `relayout_kernel<16>`: the serial baseline's standalone copy.\n",
+          summary("trace", f"trace_{workload}"),
+          f"One fused call = {' + '.join(f'{avg_s[n] * 1e3:.4f}' for n in fused)} = {call_s * 1e3:.4f} ms "
+          f"under the tracer; {flop:.4g} algorithmic FLOP per call -> {flop / call_s / 1e12:.1f} TFLOP/s "
+          f"(bench.py, HIP events around the call: {bj['roofline']['mean_launch_ms']:.4f} ms, "
+          f"{bj['roofline']['achieved']:.1f} TFLOP/s)."]
+    with open(f"{stem}_kernel_trace.md", "w") as f:
+        f.write("\n".join(tr) + "\n")
+
+    cm = [f"# Fused kernel on the {title} ({shape}): hardware counters\n",
+          "Commands (one rocprofv3 pass each; the FETCH/WRITE passes also run one 1 GiB device copy "
+          "for calibration):\n", "```"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cm.append(f"rocprofv3 --pmc {c} --output-format csv -d {d}/pmc_{c}_{workload} -o run -- "
+                  f"{short} --copy-calibration-mib 1024")
+    cm.append(f"rocprofv3 --pmc {sq1} --kernel-include-regex fa_fwd --output-format csv "
+              f"-d {d}/pmc_sq1_{workload} -o run -- {short}")
+    cm.append(f"rocprofv3 --pmc {sq2} --kernel-include-regex fa_fwd --output-format csv "
+              f"-d {d}/pmc_sq2_{workload} -o run -- {short}")
+    cm.append(f"python bench.py --summarize counters <dir>   # for each directory above")
+    cm.append(f"python bench.py --summarize report:{workload} {d}   # this file")
+    cm.append("```\n")
+    cm.append(f"Kernel source sha256/16: {hsh}. Rows of the plain-layout twin (StoreMode 1) and of "
+              "other kernels omitted.\n")
+    cm.append("## HBM traffic (KiB per dispatch)\n")
+    cm.append(fused_only(summary("counters", f"pmc_FETCH_SIZE_{workload}")) + "\n")
+    cm.append(fused_only(summary("counters", f"pmc_WRITE_SIZE_{workload}")) + "\n")
+    cm.append("## SQ counters (per dispatch, summed over the chip)\n")
+    cm.append(fused_only(summary("counters", f"pmc_sq1_{workload}")) + "\n")
+    cm.append(fused_only(summary("counters", f"pmc_sq2_{workload}")) + "\n")
+    cm.append("## Derived figures\n")
+    cm.append(f"* Calibration: the 1 GiB device copy reads FETCH_SIZE = {fe[(copy, 'FETCH_SIZE')]:.0f} KiB "
+              f"and WRITE_SIZE = {wr[(copy, 'WRITE_SIZE')]:.0f} KiB, so bytes fetched = {fscale:.3f} x "
+              f"FETCH_SIZE KiB x 1024 and bytes written = {wscale:.3f} x WRITE_SIZE KiB x 1024.")
+    cm.append(f"* HBM bytes per fused call: {bytes_call / 1e6:.1f} MB (fetched "
+              f"{sum(fetch_b.values()) / 1e6:.1f}, written {sum(write_b.values()) / 1e6:.1f}) against "
+              f"{min_bytes / 1e6:.1f} MB algorithmic (q, k, v read once, output written once); "
+              f"{bytes_call / call_s / 1e12:.3f} TB/s over the call, "
+              f"{100 * bytes_call / call_s / (HBM_PEAK_GBS * 1e9):.1f}% of 8 TB/s.")
+    n_mfma = sum(c2.get((n, "SQ_INSTS_MFMA"), 0.0) for n in fused)
+    if n_mfma:
+        cm.append(f"* SQ_INSTS_MFMA over the call x 32768 FLOP per 32x32x16 MFMA = {n_mfma * 32768:.4g} "
+                  f"FLOP issued against {flop:.4g} algorithmic ({100 * (n_mfma * 32768 / flop - 1):+.1f}%: "
+                  "keys padded to 64-key stages, the unused QK^T of the stage past the end, and for "
+                  "masked calls the 128-key tiles kept but partly outside the sequence).")
+    for n in fused:
+        short_n = n.split("(fa::FwdParams)")[0].replace("void fa::", "")
+        grbm = c2.get((n, "GRBM_GUI_ACTIVE"))
+        busy = c2.get((n, "SQ_VALU_MFMA_BUSY_CYCLES"))
+        if grbm is None or busy is None:
+            continue
+        cyc = grbm / 8.0
+        clk = cyc / avg_s[n]
+        mf = busy / 1024.0
+        co = c2[(n, "SQ_VALU_MFMA_COEXEC_CYCLES")] / busy if busy else 0.0
+        cm.append(f"* `{short_n}`: {avg_s[n] * 1e3:.4f} ms per dispatch; GRBM_GUI_ACTIVE / 8 XCDs = "
+                  f"{cyc:.4g} cycles -> {clk / 1e9:.2f} GHz held; matrix cores busy "
+                  f"{100 * mf / cyc:.1f}% of those cycles per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024 "
+                  f"SIMDs); VALU co-issued in {100 * co:.0f}% of MFMA cycles; "
+                  f"SQ_LDS_BANK_CONFLICT = {c2[(n, 'SQ_LDS_BANK_CONFLICT')]:.0f}; fetched "
+                  f"{fetch_b[n] / 1e6:.1f} MB, written {write_b[n] / 1e6:.1f} MB.")
+    with open(f"{stem}_counters.md", "w") as f:
+        f.write("\n".join(cm) + "\n")
+    rec = {"workload": workload, "kernel_source_sha256_16": hsh,
+           "kernels": {n: {"avg_ms": avg_s[n] * 1e3, "fetch_size_kib": fe[(n, "FETCH_SIZE")],
+                           "write_size_kib": wr[(n, "WRITE_SIZE")]} for n in fused},
+           "fetch_scale": fscale, "write_scale": wscale, "hbm_bytes_per_launch": round(bytes_call),
+           "launch": "one fused call: every StoreMode-0 kernel it launches",
+           "source": os.path.relpath(f"{stem}_counters.md", ROOT)}
+    with open(f"{stem}_counters.json", "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"{stem}: {bytes_call:.0f} bytes per call, {call_s * 1e3:.4f} ms")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,13 +426,20 @@ def main():
     ap.add_argument("--overhead-pairs", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the ~1.5 s shader-clock sampling window (profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB")
     ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIR"),
-                    help="print a summary of rocprofv3 CSV output (KIND: trace|counters)")
+                    help="print a summary of rocprofv3 CSV output (KIND: trace|counters), or "
+                         "write a workload's profiles/ summaries (KIND: report:<workload>)")
     a = ap.parse_args()
     if a.summarize:
-        summarize(*a.summarize)
+        kind, path = a.summarize
+        if kind.startswith("report:"):
+            write_profile_report(kind.split(":", 1)[1], path)
+        else:
+            summarize(kind, path)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -372,9 +542,11 @@ def main():
 
     achieved = flop / (mean_launch_ms * 1e-3) / 1e12
     traffic = load_traffic(a.workload)
-    clock = ClockSampler()
-    clock.window(fused, mean_launch_ms * 1e-3)
-    clk = clock.summary(achieved)
+    clk = {"sclk_mhz": None, "samples": 0, "error": "not sampled (--no-clock)"}
+    if not a.no_clock:
+        clock = ClockSampler()
+        clock.window(fused, mean_launch_ms * 1e-3)
+        clk = clock.summary(achieved)
     out = {
         "metric": "fused attn+relayout TFLOP/s at 1 GPU; % bf16 MFMA peak; fused-store overhead %",
         "value": round(tflops, 2),
