@@ -41,13 +41,15 @@ WORKLOAD_KEYS = {"video": "video-dit-share", "long": "long-video-share",
 
 
 # What one fused call launches on its stream (the roofline's "launch" is that
-# call: HIP events bracket it).  Dense: the 8-wave kernel over whole 256-query
-# tiles, plus, when the last round would fill at most half of the CUs, a second
-# launch of its split-key variant for that round.  Masked: the 4-wave kernel.
-KERNEL_LABEL = {
-    True: "fa_fwd_pp_kernel<128, Slab> (whole 256-query tiles; split-key half tiles for a short last round)",
-    False: "fa_fwd_kernel<128, Slab> (4-wave, block mask)",
-}
+# call: HIP events bracket it).  Dense: the kernel over whole 256-query tiles,
+# plus, when the last round would fill at most half of the CUs, a second
+# launch of its split-key form for that round.  Masked: one launch of the
+# split-key form over 128-query tiles (one mask row each).
+def kernel_label(D: int, dense: bool) -> str:
+    if dense:
+        return (f"fa_fwd_pp_kernel<{D}, Slab> (whole 256-query tiles; split-key half tiles "
+                "for a short last round)")
+    return f"fa_fwd_pp_kernel<{D}, Slab, masked> (split-key 128-query tiles, kept mask tiles only)"
 
 
 def kernel_source_hash() -> str:
@@ -60,10 +62,8 @@ def kernel_source_hash() -> str:
 
 def profile_prefix(workload: str) -> str:
     """File-name stem of a workload's rocprofv3 summaries under profiles/: the
-    kernel family that runs it, then the workload."""
-    import workloads as wl
-    fam = "fa_fwd_quad" if wl.WORKLOADS[workload].keep_prob is not None else "fa_fwd_pp"
-    return f"{fam}_{workload}"
+    kernel, then the workload."""
+    return f"fa_fwd_pp_{workload}"
 
 
 def load_traffic(workload: str):
@@ -340,10 +340,11 @@ def write_profile_report(workload: str, d: str):
           f"python bench.py --summarize trace {d}/trace_{workload}",
           "```\n",
           f"Kernel source sha256/16: {hsh}. StoreMode 0 = slab (fused re-layout), 1 = plain "
-          "[B][H][S][D] (the overhead twin and the serial baseline's attention). For fa_fwd_pp_kernel "
-          "the last template flag is false for whole 256-query tiles and true for split-key half tiles "
-          "(a short last round, second launch on the same stream); fa_fwd_kernel is the 4-wave kernel "
-          "that runs masked calls. `relayout_kernel<16>`: the serial baseline's standalone copy.\n",
+          "[B][H][S][D] (the overhead twin and the serial baseline's attention). The last two "
+          "template flags of fa_fwd_pp_kernel: split-key units, masked units (false, false: whole "
+          "256-query tiles; true, false: split-key half tiles of a short last round, a second launch "
+          "on the same stream; true, true: masked 128-query tiles). `relayout_kernel<16>`: the "
+          "serial baseline's standalone copy.\n",
           summary("trace", f"trace_{workload}"),
           f"One fused call = {' + '.join(f'{avg_s[n] * 1e3:.4f}' for n in fused)} = {call_s * 1e3:.4f} ms "
           f"under the tracer; {flop:.4g} algorithmic FLOP per call -> {flop / call_s / 1e12:.1f} TFLOP/s "
@@ -571,7 +572,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": KERNEL_LABEL[mask is None],
+                     "kernel": kernel_label(w.D, mask is None),
                      "mean_launch_ms": round(mean_launch_ms, 4),
                      "launch_ms_p10_p50_p90": [round(float(np.percentile(launch_ms, x)), 4)
                                                for x in (10, 50, 90)]},

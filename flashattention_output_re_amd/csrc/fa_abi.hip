@@ -73,9 +73,10 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
         int S, int D, int P, float scale, const uint64_t* mask, hipStream_t stream) {
   const int st = validate(q, k, v, out, B, H, S, D, P, scale, mask);
   if (st != FA_OK) return st;
-  // Dense attention runs on the 8-wave ping-pong kernel; a block mask gives
-  // each 128-query tile its own key set, so it runs on the 4-wave kernel.
-  const fa::Variant var = mask ? fa::Variant::Quad : fa::Variant::PingPong;
+  // Dense attention runs on 256-query tiles; a block mask gives each
+  // 128-query tile its own key set, so masked calls run on 128-query tiles
+  // with the keys split between the two wave groups.
+  const fa::Variant var = mask ? fa::Variant::Masked : fa::Variant::Whole;
   const int cap = grid_cap_for(D, mode, var);
   if (cap <= 0) return FA_EDEVICE;
   fa::FwdParams p;
@@ -100,7 +101,7 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   // that |s| * c rounds away against 1 gives the same weights bit for bit,
   // and keeps (-inf) * c = -inf for the keys past S.
   if (p.c == 0.0f) p.c = 1e-30f;
-  if (var == fa::Variant::Quad)
+  if (mask)
     return fa::launch_fwd(D, mode, var, p, cap, stream) == 0 ? FA_OK : FA_ELAUNCH;
 
   // Dense: whole 256-query tiles fill `cap` CUs per round.  When the last
@@ -111,7 +112,7 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   const int stages = (S + 63) / 64;
   if (tail == 0 || 2 * tail > cap || stages < 2)
     return fa::launch_fwd(D, mode, var, p, cap, stream) == 0 ? FA_OK : FA_ELAUNCH;
-  const int split_cap = grid_cap_for(D, mode, fa::Variant::PingPongSplit);
+  const int split_cap = grid_cap_for(D, mode, fa::Variant::Split);
   if (split_cap <= 0) return FA_EDEVICE;
   fa::FwdParams whole = p;
   whole.units = p.units - tail;
@@ -119,7 +120,7 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   fa::FwdParams half = p;
   half.units = 2 * tail;
   half.unit_base = p.units - tail;
-  return fa::launch_fwd(D, mode, fa::Variant::PingPongSplit, half, split_cap, stream) == 0
+  return fa::launch_fwd(D, mode, fa::Variant::Split, half, split_cap, stream) == 0
              ? FA_OK : FA_ELAUNCH;
 }
 

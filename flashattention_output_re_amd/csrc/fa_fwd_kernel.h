@@ -7,13 +7,14 @@ namespace fa {
 
 enum class StoreMode : int { Slab = 0, Plain = 1 };
 
-// Workgroup shapes.  Quad: 4 waves own 128 queries, two workgroups per CU,
-// any mask.  PingPong: 8 waves own 256 queries and share one K/V stream, one
-// workgroup per CU, dense attention only.  PingPongSplit: the same 8 waves own
-// one 128-query half of a 256-query tile and split its keys between the two
-// wave groups (for the last, partial round of a dense launch).
-enum class Variant : int { Quad = 0, PingPong = 1, PingPongSplit = 2 };
-constexpr int tile_rows(Variant v) { return v == Variant::Quad ? 128 : 256; }
+// Forms of the kernel (8 waves, one workgroup per CU).  Whole: 256-query
+// tiles, the two wave groups holding 128 queries each and sharing one K/V
+// stream (dense attention).  Split: one 128-query half of a 256-query tile,
+// its keys split between the two groups (the last, partial round of a dense
+// launch).  Masked: the split form on 128-query tiles, one mask row each,
+// each group streaming half of the row's kept 128-key tiles.
+enum class Variant : int { Whole = 0, Split = 1, Masked = 2 };
+constexpr int tile_rows(Variant v) { return v == Variant::Masked ? 128 : 256; }
 
 // Kernel arguments, passed by value.  Every tensor is bf16 stored as uint16_t.
 struct FwdParams {
@@ -25,7 +26,8 @@ struct FwdParams {
   int B, H, S, P, Sp;    // Sp = S / P
   int nqt;               // output tiles (tile_rows queries) per (b, h)
   int units;             // work units of this launch (see unit_base)
-  int unit_base;         // PingPongSplit: unit u is half u % 2 of tile unit_base + u / 2
+  int unit_base;         // Split: unit u is half u % 2 of tile unit_base + u / 2
+                         // (Whole, Masked: unit u is tile u)
   int nmt;               // 128-key mask tiles per row (= nqt)
   int mw;                // 64-bit words per mask row
   float c;               // scale * log2(e)

@@ -10,15 +10,14 @@
 // the next tile's Q-loop; no dedicated communication wavefront).
 // StoreMode::Plain runs the same body but writes [B][H][S][D].
 //
-// Two kernels:
-//   fa_fwd_pp_kernel (dense): 8 waves, one workgroup per CU, 256-query tiles,
-//   softmax and MFMA work in separate regions run by two wave groups in
-//   alternation (its own header comment below has the schedule).
-//   fa_fwd_kernel (block mask): 4 waves, two workgroups per CU, 128-query
-//   tiles (one mask row), the next stage's QK^T MFMAs interleaved with the
-//   current stage's softmax inside each wave.
+// One kernel, fa_fwd_pp_kernel: 8 waves, one workgroup per CU, softmax and
+// MFMA work in separate regions run by two wave groups in alternation (its
+// own header comment below has the schedule), in three forms: whole
+// 256-query tiles (dense), split-key 128-query half tiles (the last, partial
+// round of a dense launch) and split-key 128-query tiles over the kept tiles
+// of one mask row (block-sparse).
 //
-// Layout choices (per wavefront, 32 queries), shared by both:
+// Layout choices (per wavefront, 32 queries):
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims of K from
 //   LDS, B = 16 dims x 32 queries of Q held in VGPRs.  The accumulator puts one
 //   query per lane (lane % 32) and 16 keys per lane, so a row's max and sum are
@@ -52,22 +51,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
 constexpr int BM = 128;          // queries per output tile (= mask tile)
 constexpr int BN = 64;           // keys per LDS stage
 constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
-// Tuning knobs, overridable at build time (-D): operand reads issued ahead of
-// their MFMA in the 4-wave kernel (K, V) and in the ping-pong kernel's MFMA
-// region, and waves per SIMD of the 4-wave kernel.
-#ifndef FA_KLEAD
-#define FA_KLEAD 3
-#endif
-#ifndef FA_VLEAD
-#define FA_VLEAD 4
-#endif
-#ifndef FA_WAVES_PER_EU
-#define FA_WAVES_PER_EU 2
-#endif
+// Tuning knob, overridable at build time (-D): operand reads issued ahead of
+// their MFMA in the MFMA region.
 #ifndef FA_MLEAD
 #define FA_MLEAD 3
 #endif
@@ -129,31 +117,11 @@ template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Tile<
 // per 16 lanes; XOR the chunk by 4 * (row % 4).
 template <int D> __device__ __forceinline__ int v_swz(int r) { return (4 * (r & 3)) & (Tile<D>::CH - 1); }
 
-// One K (SWZ_V = false) or V (true) stage of BN keys starting at key0 into
-// `buf`; keys past S come back as zeros.  Each wave issues CH/4 instructions.
+// LDS-DMA instructions (1 KiB each) that each of four waves issues to move
+// one K or V stage of BN keys.
 template <int D> struct Dma {
-  static constexpr int PER_WAVE4 = BN * Tile<D>::CH / (4 * 64);   // instructions per wave (4 waves)
+  static constexpr int PER_WAVE4 = BN * Tile<D>::CH / (4 * 64);
 };
-
-// One K (SWZ_V = false) or V (true) stage of BN keys starting at key0 into
-// `buf`, shared by four waves (`wave` in [0, 4)); keys past S come back as
-// zeros.  Each wave issues Dma<D>::PER_WAVE4 instructions.
-template <int D, bool SWZ_V>
-__device__ __forceinline__ void stage_dma(uint16_t* buf, __amdgpu_buffer_rsrc_t r, int key0,
-                                          int wave, int lane) {
-  constexpr int CH = Tile<D>::CH;
-  constexpr int PER_WAVE = Dma<D>::PER_WAVE4;
-#pragma unroll
-  for (int q = 0; q < PER_WAVE; ++q) {
-    const int blk = PER_WAVE * wave + q;           // 64-chunk block of the stage
-    const int pos = 64 * blk + lane;               // chunk position written by this lane
-    const int row = pos / CH, pc = pos % CH;
-    const int lc = pc ^ (SWZ_V ? v_swz<D>(row) : k_swz<D>(row));   // logical chunk
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(buf + 64 * 8 * blk), 16,
-        (uint32_t)((key0 + row) * D * 2 + lc * 16), 0, 0, 0);
-  }
-}
 
 // N consecutive 1 KB blocks of a K or V stage into LDS from `dst` on:
 // instruction i moves 16 bytes per lane from byte offset base + off[i] of r
@@ -253,32 +221,49 @@ __device__ __forceinline__ int xcd_slot(int block, int G) {
   return (G % 8 == 0) ? (block % 8) * (G / 8) + block / 8 : block;
 }
 
-// Iterates the K/V stages (BN keys each) a query tile attends to: all stages
-// for dense attention, or the stages of the kept 128-key mask tiles.
-struct StageIter {
-  const uint64_t* row;   // mask row (nullptr = dense)
-  int S, nmt, mw;
-  __device__ int first() const {
-    if (!row) return 0;
-    return next_tile(0);
-  }
-  __device__ int next_tile(int mt) const {             // first kept mask tile >= mt, as a stage
-    if (mt >= nmt) return -1;
-    int w = mt >> 6;
-    uint64_t bits = row[w] & (~0ull << (mt & 63));
-    while (bits == 0) {
-      if (++w >= mw) return -1;
-      bits = row[w];
+// The 64-key stages of one mask row's kept 128-key tiles, in key order (two
+// stages per tile), as one of two streams: stream 0 takes the first half of
+// the row's 2K stages, stream 1 the second.  next() gives the first key of
+// the stream's next stage, or S once the stream's K stages are used up.  Bits
+// for tiles past the row's end are ignored.  All state is wave-uniform.
+struct KeptStages {
+  const uint64_t* row;
+  int mw, w, half, left, S;
+  uint64_t bits, last_mask;
+
+  __device__ uint64_t word(int i) const { return i == mw - 1 ? row[i] & last_mask : row[i]; }
+
+  // Positions the stream; returns K, the number of kept tiles in the row.
+  __device__ int init(const uint64_t* r, int nmt, int words, int seq, int stream) {
+    row = r;
+    mw = words;
+    S = seq;
+    last_mask = (nmt & 63) ? (1ull << (nmt & 63)) - 1 : ~0ull;
+    int kept = 0;
+    for (int i = 0; i < mw; ++i) kept += __builtin_popcountll(word(i));
+    // Stream 1 starts at stage K: skip K / 2 tiles and, for odd K, the first
+    // half of the next one.
+    int skip = stream ? kept >> 1 : 0;
+    w = 0;
+    bits = word(0);
+    while (skip >= __builtin_popcountll(bits) && skip > 0) {
+      skip -= __builtin_popcountll(bits);
+      bits = word(++w);
     }
-    const int t = (w << 6) + __builtin_ctzll(bits);
-    return t < nmt ? 2 * t : -1;
+    for (; skip > 0; --skip) bits &= bits - 1;
+    half = stream ? (kept & 1) : 0;
+    left = kept;
+    return kept;
   }
-  __device__ int next(int st) const {
-    if (st < 0) return -1;
-    const int nx = st + 1;
-    if (nx * BN >= S) return -1;
-    if (!row || (nx & 1)) return nx;                   // dense, or the second half of a mask tile
-    return next_tile(nx >> 1);
+
+  __device__ int next() {
+    if (left <= 0) return S;
+    --left;
+    while (bits == 0) bits = word(++w);
+    const int key = ((w << 6) + __builtin_ctzll(bits)) * BM + half * BN;
+    if (half) bits &= bits - 1;
+    half ^= 1;
+    return key;
   }
 };
 
@@ -330,73 +315,13 @@ __device__ __forceinline__ void qk_mfma(f32x16 (&s)[2], const uint16_t* ks,
   }
 }
 
-// Online softmax of one K/V stage, cut into NA pieces that interleave with
-// the NA MFMAs of the region it runs in (piece `seg` follows MFMA `seg`).
-// This lane holds 32 scores of its query (two 32-key blocks x 16).  Pieces
-// [0, NMAX) reduce the row extreme (max for c > 0, min for c < 0), piece NMAX
-// updates the running max, the next NEXP pieces compute the probabilities
-// exp2(s c - m) as bf16 pairs (the B operand of the PV MFMAs) and their sum,
-// and the last piece folds that sum into the running row sum.  The running
-// max is raised only when some row of the wave exceeds it by more than kTau.
-template <bool NEG, int NA>
-struct StageSoftmax {
-  static constexpr int NMAX = NA >= 16 ? 2 : 1;
-  static constexpr int NEXP = NA - NMAX - 2;
-  float e0 = 0.0f, e1 = 0.0f, neg_m = 0.0f, alpha = 1.0f, lsum = 0.0f;
-  bool rescale = false;
-  uint32_t pk[16];
-
-  __device__ __forceinline__ void piece(int seg, const f32x16 (&sc)[2], float c, float& m_run,
-                                        float& l_run) {
-    if (seg < NMAX) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        if (NMAX == 2 && mb != seg) continue;
-        float e = sc[mb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) e = NEG ? fminf(e, sc[mb][r]) : fmaxf(e, sc[mb][r]);
-        if (mb == 0) e0 = e; else e1 = e;
-      }
-    } else if (seg == NMAX) {
-      float e = NEG ? fminf(e0, e1) : fmaxf(e0, e1);
-      e = NEG ? halves_min(e) : halves_max(e);
-      const float m_cand = fmaxf(m_run, e * c);
-      rescale = __builtin_amdgcn_ballot_w64(m_cand > m_run + kTau) != 0;
-      const float m_use = rescale ? m_cand : m_run;
-      alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_use;
-      neg_m = -m_use;
-    } else if (seg < NMAX + 1 + NEXP) {
-      const int k = seg - NMAX - 1;
-#pragma unroll
-      for (int pi = (16 * k) / NEXP; pi < (16 * (k + 1)) / NEXP; ++pi) {
-        const int mb = pi >> 3, r = 2 * (pi & 7);
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r], c, neg_m));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r + 1], c, neg_m));
-        lsum += x0;
-        lsum += x1;
-        pk[pi] = pack_bf16(x0, x1);
-        // Pin the value here: keeps the exp2 work inside this piece instead
-        // of letting it sink past the rescale branch that follows the region.
-        asm volatile("" ::"v"(pk[pi]));
-      }
-    } else {
-      l_run = l_run * alpha + lsum;
-      asm volatile("" ::"v"(l_run));
-    }
-  }
-
-  // B operand of the PV MFMA over 16-key step kk.
-  __device__ __forceinline__ bf16x8 p_operand(int kk) const {
-    return __builtin_bit_cast(bf16x8, u32x4{pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]});
-  }
-};
-
-// Online softmax of one K/V stage as one block of VALU work (the ping-pong
-// kernel runs it in a region of its own, beside another wave's MFMAs).  The
-// same arithmetic as StageSoftmax, with independent chains for the scheduler:
-// the row extreme over four partial chains, all 32 probabilities, the row sum
-// over four partial sums (fp32 addition in a different order).
+// Online softmax of one K/V stage as one block of VALU work, run in a region
+// of its own beside another wave's MFMAs.  This lane holds 32 scores of its
+// query (two 32-key blocks x 16).  The row extreme (max for c > 0, min for
+// c < 0) over four partial chains, the running max raised only when some row
+// of the wave exceeds it by more than kTau, all 32 probabilities
+// exp2(s c - m) as bf16 pairs (the B operand of the PV MFMAs), and their sum
+// over four partial sums folded into the running row sum.
 template <bool NEG>
 struct StageProbs {
   float alpha = 1.0f;
@@ -494,154 +419,7 @@ __device__ __forceinline__ void store_tile(const FwdParams& p, const f32x16 (&ac
   }
 }
 
-template <int D, StoreMode MODE, bool NEG>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(FA_WAVES_PER_EU, FA_WAVES_PER_EU)))
-void fa_fwd_kernel(FwdParams p) {
-  constexpr int NKS = D / 16;     // QK^T contraction steps
-  constexpr int NDB = D / 32;     // 32-dim blocks of O^T
-  // Four separate LDS objects (K and V, double buffered) so that the compiler
-  // can tell a DMA into one buffer from reads of another and does not wait
-  // for the DMA before those reads.
-  __shared__ __attribute__((aligned(16))) uint16_t kb0[Tile<D>::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t kb1[Tile<D>::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t vb0[Tile<D>::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t vb1[Tile<D>::ELEMS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-  const float c = p.c;
-  const float fill = NEG ? __builtin_inff() : -__builtin_inff();   // fill * c = -inf
-  const uint32_t head_bytes = (uint32_t)p.S * D * 2;
-
-  // Plain order here: on the 30%-dense block mask the XCD-aware order
-  // measured about 18% slower for this kernel (its workgroups skip different
-  // tiles, so they do not stream K/V in step the way dense tiles do).
-  const int slot_id = blockIdx.x;
-  for (int base = 0; base + slot_id < p.units; base += gridDim.x) {
-    const int unit = base + slot_id;
-    const int bh = unit / p.nqt, qt = unit - bh * p.nqt;
-    const int b = bh / p.H, h = bh - b * p.H;
-    const size_t head_off = (size_t)bh * p.S * D;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_off, head_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, head_bytes);
-
-    // This lane's query and its B operand of S^T = K Q^T (8 dims per step).
-    const int qrow = qt * BM + wave * 32 + l32;
-    bf16x8 qf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, load16(rq, (uint32_t)(qrow * D * 2 + ks * 32 + g * 16)));
-
-    f32x16 acc[NDB];
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-    float m_run = -__builtin_inff();
-    float l_run = 0.0f;
-
-    const StageIter it{p.mask ? p.mask + ((size_t)h * p.nmt + qt) * p.mw : nullptr, p.S, p.nmt,
-                       p.mw};
-    int st0 = it.first();
-    int st1 = it.next(st0);
-
-    // Prologue: K and V of the first stage, K of the second, scores of the first.
-    f32x16 s_cur[2] = {f32x16{}, f32x16{}};
-    if (st0 >= 0) {
-      stage_dma<D, false>(kb0, rk, st0 * BN, wave, lane);
-      stage_dma<D, true>(vb0, rv, st0 * BN, wave, lane);
-      if (st1 >= 0) stage_dma<D, false>(kb1, rk, st1 * BN, wave, lane);
-    }
-    wait_dma();
-    __syncthreads();
-    if (st0 >= 0) qk_mfma<D>(s_cur, kb0, qf, l32, g);
-    __syncthreads();   // every wave is done with K buffer 0 before it is refilled
-
-    // One K/V stage, software-pipelined: region A computes the softmax of the
-    // current scores (sc) while the MFMAs produce the next stage's scores (sn);
-    // region B runs PV of the current stage and stages the following K/V
-    // tiles into LDS.  Called with the two score tiles alternating so that no
-    // copy between them is needed.
-    // PAR is the parity of the stage's sequence number: stage n reads K of
-    // the next stage from kb[(n + 1) % 2] and V from vb[n % 2], and refills
-    // kb[n % 2] (K two ahead) and vb[(n + 1) % 2] (V one ahead).
-    auto step = [&](auto PAR, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-      constexpr int par = decltype(PAR)::value;
-      uint16_t* const k_fill = par ? kb1 : kb0;
-      const uint16_t* const kn = par ? kb0 : kb1;
-      uint16_t* const v_fill = par ? vb0 : vb1;
-      const uint16_t* const vt = par ? vb1 : vb0;
-      const int st2 = it.next(st1);
-      // LDS DMA for the stages after this one, into the buffers the previous
-      // stage freed: K two ahead, V one ahead.  A stage that does not exist is
-      // read at key S, which the buffer resource returns as zeros; its LDS
-      // copy is never used.
-      stage_dma<D, false>(k_fill, rk, (st2 >= 0 ? st2 * BN : p.S), wave, lane);
-      stage_dma<D, true>(v_fill, rv, (st1 >= 0 ? st1 * BN : p.S), wave, lane);
-
-      mask_tail(sc, st0 * BN, p.S, g, fill);
-
-      // ---- region A.  After the last stage the QK^T MFMAs read a stale K
-      // buffer and their result is dropped, which keeps the region branch-free.
-      constexpr int NA = 2 * NKS;                  // QK^T MFMAs of the next stage
-      constexpr int NB = 4 * NDB;                  // PV MFMAs of this stage
-      constexpr int KLEAD = FA_KLEAD;              // K operand reads issued ahead
-      constexpr int VLEAD = FA_VLEAD;              // V operand reads issued ahead
-      // MFMA i of region A: key block i & 1, dims 16 * (i >> 1).
-      auto ka_read = [&](int i) { return k_operand<D>(kn, i & 1, i >> 1, l32, g); };
-      // MFMA j of region B: key step j / NDB, dim block j % NDB.
-      auto va_read = [&](int j) { return v_operand<D>(vt, j / NDB, j % NDB, lane); };
-      bf16x8 ka[NA];
-      bf16x8 va[NB];
-#pragma unroll
-      for (int i = 0; i < KLEAD; ++i) ka[i] = ka_read(i);
-      sn[0] = f32x16{};
-      sn[1] = f32x16{};
-      StageSoftmax<NEG, NA> sm;
-#pragma unroll
-      for (int seg = 0; seg < NA; ++seg) {
-        if (seg + KLEAD < NA) ka[seg + KLEAD] = ka_read(seg + KLEAD);
-        if (seg >= NA - VLEAD) va[seg - (NA - VLEAD)] = va_read(seg - (NA - VLEAD));
-        sn[seg & 1] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[seg], qf[seg >> 1], sn[seg & 1], 0, 0, 0);
-        sm.piece(seg, sc, c, m_run, l_run);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      // ---- region B: PV of this stage, then LDS staging of the next stages.
-      if (sm.rescale) {
-#pragma unroll
-        for (int i = 0; i < NDB; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][r] *= sm.alpha;
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (j + VLEAD < NB) va[j + VLEAD] = va_read(j + VLEAD);
-        acc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], sm.p_operand(j / NDB),
-                                                               acc[j % NDB], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      wait_dma();
-      __syncthreads();
-
-      st0 = st1;
-      st1 = st2;
-    };
-
-    f32x16 s_alt[2];
-    while (st0 >= 0) {
-      step(std::integral_constant<int, 0>{}, s_cur, s_alt);
-      if (st0 < 0) break;
-      step(std::integral_constant<int, 1>{}, s_alt, s_cur);
-    }
-
-    store_tile<D, MODE>(p, acc, l_run, qrow, b, h, bh, g);
-  }
-}
-
-// Ping-pong kernel for dense attention: 8 waves, one workgroup per CU.
+// Ping-pong kernel: 8 waves, one workgroup per CU.
 // Waves 0-3 form group 0 and waves 4-7 group 1; the SIMD that runs wave w
 // also runs wave w + 4.  Each K/V stage n of a wave is split into two regions
 // separated by workgroup barriers: region S(n), the online softmax of the
@@ -677,10 +455,16 @@ void fa_fwd_kernel(FwdParams p) {
 // stage n and V stage n + 1 into the slot of V stage n - 1 (both last read in
 // M(n - 1)), both first read in M(n + 1).  At the end group 1 hands its
 // partial (max, sum, O) to group 0 through LDS, which merges and stores.
-template <int D, StoreMode MODE, bool NEG, bool SPLIT>
+//
+// Masked units (MASKED = true, split-key) are the 128-query tiles of a block
+// mask: the row's K kept 128-key tiles give 2K stages in key order, group 0
+// takes the first K and group 1 the rest (KeptStages), with the split
+// schedule above; tiles the mask drops are never loaded.
+template <int D, StoreMode MODE, bool NEG, bool SPLIT, bool MASKED = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_pp_kernel(FwdParams p) {
+  static_assert(!MASKED || SPLIT, "masked units are split-key units");
   constexpr int NKS = D / 16;     // QK^T contraction steps
   constexpr int NDB = D / 32;     // 32-dim blocks of O^T
   constexpr int NA = 2 * NKS;     // QK^T MFMAs per stage
@@ -709,9 +493,8 @@ void fa_fwd_pp_kernel(FwdParams p) {
   const float c = p.c;
   const float fill = NEG ? __builtin_inff() : -__builtin_inff();   // fill * c = -inf
   const uint32_t head_bytes = (uint32_t)p.S * D * 2;
-  const int ns = (p.S + BN - 1) / BN;                               // K/V stages
+  const int ns = (p.S + BN - 1) / BN;                               // K/V stages (dense)
   const int nsh = (ns + 1) / 2;                                     // stages per stream (SPLIT)
-  const int nloop = SPLIT ? nsh : ns;
   const int own = SPLIT ? grp : 0;   // the stream this wave computes on and (SPLIT) loads
   // Stage j of this wave's stream starts at key key_of(j); a stage past the
   // end is read at key S, which the buffer returns as zeros.
@@ -736,23 +519,42 @@ void fa_fwd_pp_kernel(FwdParams p) {
     voff[q] = dma_lane_off<D, true>(wq, lane, q);
   }
 
-  const int slot_id = xcd_slot(blockIdx.x, gridDim.x);
+  // Dense units in XCD-aware order.  Masked units keep the plain order: on a
+  // 30%-dense block mask the XCD-aware order measured slower (its workgroups
+  // skip different tiles, so they do not stream K/V in step as dense tiles
+  // do).
+  const int slot_id = MASKED ? (int)blockIdx.x : xcd_slot(blockIdx.x, gridDim.x);
   for (int base = 0; base + slot_id < p.units; base += gridDim.x) {
     const int unit = base + slot_id;
-    const int tile = SPLIT ? p.unit_base + (unit >> 1) : unit;     // 256-query tile
+    // Dense: 256-query tile `tile` (split units: its half unit & 1).  Masked:
+    // 128-query tile qt of head bh, which is mask row qt.
+    const int tile = MASKED ? unit : SPLIT ? p.unit_base + (unit >> 1) : unit;
     const int bh = tile / p.nqt, qt = tile - bh * p.nqt;
     const int b = bh / p.H, h = bh - b * p.H;
     const size_t head_off = (size_t)bh * p.S * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_off, head_bytes);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, head_bytes);
-    // This wave's share of K stage j into slot `slot`, and of V stage j.
-    // This wave's share of K or V stage j into slot `slot`.
-    auto dma_k = [&](int slot, int j) {
-      dma_blocks<PW>(kbuf(slot) + 64 * 8 * PW * wq, rk, (uint32_t)key_of(j) * (D * 2), koff);
+    // Masked units: this group's stream of kept stages, and the first keys of
+    // stages n, n + 1 and n + 2 of the stream (key_n[0..2]), advanced after
+    // each stage.
+    KeptStages kept;
+    int key_n[3] = {0, 0, 0};
+    int nloop = SPLIT ? nsh : ns;
+    if (MASKED) {
+      nloop = kept.init(p.mask + ((size_t)h * p.nmt + qt) * p.mw, p.nmt, p.mw, p.S, own);
+      key_n[0] = kept.next();
+      key_n[1] = kept.next();
+      key_n[2] = kept.next();
+    }
+    // First key of stage j of this wave's stream.
+    auto stage_key = [&](int j) { return MASKED ? key_n[j] : key_of(j); };
+    // This wave's share of the K or V stage that starts at key `key` into slot `slot`.
+    auto dma_k = [&](int slot, int key) {
+      dma_blocks<PW>(kbuf(slot) + 64 * 8 * PW * wq, rk, (uint32_t)key * (D * 2), koff);
     };
-    auto dma_v = [&](int slot, int j) {
-      dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key_of(j) * (D * 2), voff);
+    auto dma_v = [&](int slot, int key) {
+      dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key * (D * 2), voff);
     };
     // The DMA issued at the start of region S(n) (SLOT = n % NBUF), after
     // the barrier that ends every wave's reads of the slots it refills.
@@ -763,17 +565,18 @@ void fa_fwd_pp_kernel(FwdParams p) {
     auto stage_dma = [&](auto SLOT, int n) {
       constexpr int slot = decltype(SLOT)::value;
       if (SPLIT) {
-        dma_k(slot, n + 2);
-        dma_v((slot + 1) % NBUF, n + 1);
+        dma_k(slot, MASKED ? key_n[2] : key_of(n + 2));
+        dma_v((slot + 1) % NBUF, MASKED ? key_n[1] : key_of(n + 1));
       } else if (grp == 0) {
-        dma_k((slot + 2) % NBUF, n + 2);
+        dma_k((slot + 2) % NBUF, key_of(n + 2));
       } else {
-        dma_v((slot + 2) % NBUF, n + 2);
+        dma_v((slot + 2) % NBUF, key_of(n + 2));
       }
     };
 
-    const int qrow = SPLIT ? qt * 256 + (unit & 1) * 128 + wq * 32 + l32
-                           : qt * 256 + wave * 32 + l32;
+    const int qrow = MASKED  ? qt * BM + wq * 32 + l32
+                     : SPLIT ? qt * 256 + (unit & 1) * 128 + wq * 32 + l32
+                             : qt * 256 + wave * 32 + l32;
     bf16x8 qf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -782,21 +585,25 @@ void fa_fwd_pp_kernel(FwdParams p) {
     f32x16 acc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-    float m_run = -__builtin_inff();
+    // A masked stream may meet a stage with no key at all (the second half of
+    // a kept last tile shorter than 64 keys) before any other: a finite
+    // starting max keeps its weights exp2(-inf) = 0 rather than NaN, and is
+    // replaced by the first real maximum (the rescale factor is then 0).
+    float m_run = MASKED ? -3.0e38f : -__builtin_inff();
     float l_run = 0.0f;
 
     // Prologue: K stages 0 and 1 and V stage 0 (SPLIT: each group, its own
     // stream) or K stages 0, 1 (group 0) and V stages 0, 1 (group 1); every
     // wave computes the scores of its stream's first stage.
     if (SPLIT || grp == 0) {
-      dma_k(0, 0);
-      dma_k(1, 1);
+      dma_k(0, stage_key(0));
+      dma_k(1, stage_key(1));
     }
     if (SPLIT) {
-      dma_v(0, 0);
+      dma_v(0, stage_key(0));
     } else if (grp == 1) {
-      dma_v(0, 0);
-      dma_v(1, 1);
+      dma_v(0, stage_key(0));
+      dma_v(1, stage_key(1));
     }
     wait_dma();
     __syncthreads();
@@ -809,7 +616,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
     // then the wait for the DMA issued in S(n - 1).
     auto region_s = [&](auto SLOT, int n, StageProbs<NEG>& sm) {
       stage_dma(SLOT, n);
-      mask_tail(s, (own * nsh + n) * BN, p.S, g, fill);
+      mask_tail(s, MASKED ? key_n[0] : (own * nsh + n) * BN, p.S, g, fill);
       sm.compute(s, c, m_run, l_run);
       wait_vm<NDMA>();
     };
@@ -861,6 +668,11 @@ void fa_fwd_pp_kernel(FwdParams p) {
       barrier_keep_dma();
       region_m(SLOT, sm);
       barrier_keep_dma();
+      if (MASKED) {
+        key_n[0] = key_n[1];
+        key_n[1] = key_n[2];
+        key_n[2] = kept.next();
+      }
     };
 
     for (int n = 0; n < nloop; n += NBUF) {
@@ -916,31 +728,25 @@ void fa_fwd_pp_kernel(FwdParams p) {
   }
 }
 
+// Kernel form of each variant: split-key units, masked units.
+template <Variant VAR> constexpr bool kSplit = VAR != Variant::Whole;
+template <Variant VAR> constexpr bool kMasked = VAR == Variant::Masked;
+
 template <Variant VAR, int D, StoreMode MODE, bool NEG>
 static int launch_one(const FwdParams& p, int grid_cap, hipStream_t stream) {
   const int grid = p.units < grid_cap ? p.units : grid_cap;
-  if (VAR == Variant::PingPong)
-    hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, false>), dim3(grid), dim3(512), 0, stream, p);
-  else if (VAR == Variant::PingPongSplit)
-    hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, true>), dim3(grid), dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((fa_fwd_kernel<D, MODE, NEG>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, kSplit<VAR>, kMasked<VAR>>), dim3(grid),
+                     dim3(512), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <Variant VAR, int D, StoreMode MODE>
 static int occupancy_one(int* blocks) {
-  hipError_t e;
-  if (VAR == Variant::PingPong)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fa_fwd_pp_kernel<D, MODE, false, false>,
-                                                     512, 0);
-  else if (VAR == Variant::PingPongSplit)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fa_fwd_pp_kernel<D, MODE, false, true>,
-                                                     512, 0);
-  else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fa_fwd_kernel<D, MODE, false>,
-                                                     kThreads, 0);
-  return e == hipSuccess ? 0 : -1;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+             blocks, fa_fwd_pp_kernel<D, MODE, false, kSplit<VAR>, kMasked<VAR>>, 512, 0) ==
+                 hipSuccess
+             ? 0
+             : -1;
 }
 
 template <Variant VAR, int D>
@@ -949,16 +755,19 @@ static int occupancy_d(StoreMode mode, int* blocks) {
                                  : occupancy_one<VAR, D, StoreMode::Plain>(blocks);
 }
 
+template <Variant VAR>
+static int occupancy_v(int D, StoreMode mode, int* blocks) {
+  return D == 128 ? occupancy_d<VAR, 128>(mode, blocks) : occupancy_d<VAR, 64>(mode, blocks);
+}
+
 int kernel_occupancy(int D, StoreMode mode, Variant var, int* blocks_per_cu) {
   if (D != 64 && D != 128) return -1;
-  if (var == Variant::PingPong)
-    return D == 128 ? occupancy_d<Variant::PingPong, 128>(mode, blocks_per_cu)
-                    : occupancy_d<Variant::PingPong, 64>(mode, blocks_per_cu);
-  if (var == Variant::PingPongSplit)
-    return D == 128 ? occupancy_d<Variant::PingPongSplit, 128>(mode, blocks_per_cu)
-                    : occupancy_d<Variant::PingPongSplit, 64>(mode, blocks_per_cu);
-  return D == 128 ? occupancy_d<Variant::Quad, 128>(mode, blocks_per_cu)
-                  : occupancy_d<Variant::Quad, 64>(mode, blocks_per_cu);
+  switch (var) {
+    case Variant::Whole: return occupancy_v<Variant::Whole>(D, mode, blocks_per_cu);
+    case Variant::Split: return occupancy_v<Variant::Split>(D, mode, blocks_per_cu);
+    case Variant::Masked: return occupancy_v<Variant::Masked>(D, mode, blocks_per_cu);
+  }
+  return -1;
 }
 
 template <Variant VAR, int D, StoreMode MODE>
@@ -973,17 +782,21 @@ static int launch_d(StoreMode mode, const FwdParams& p, int grid_cap, hipStream_
                                  : launch_sign<VAR, D, StoreMode::Plain>(p, grid_cap, stream);
 }
 
+template <Variant VAR>
+static int launch_v(int D, StoreMode mode, const FwdParams& p, int grid_cap, hipStream_t stream) {
+  return D == 128 ? launch_d<VAR, 128>(mode, p, grid_cap, stream)
+                  : launch_d<VAR, 64>(mode, p, grid_cap, stream);
+}
+
 int launch_fwd(int D, StoreMode mode, Variant var, const FwdParams& p, int grid_cap,
                hipStream_t stream) {
   if (D != 64 && D != 128) return -1;
-  if (var == Variant::PingPong)
-    return D == 128 ? launch_d<Variant::PingPong, 128>(mode, p, grid_cap, stream)
-                    : launch_d<Variant::PingPong, 64>(mode, p, grid_cap, stream);
-  if (var == Variant::PingPongSplit)
-    return D == 128 ? launch_d<Variant::PingPongSplit, 128>(mode, p, grid_cap, stream)
-                    : launch_d<Variant::PingPongSplit, 64>(mode, p, grid_cap, stream);
-  return D == 128 ? launch_d<Variant::Quad, 128>(mode, p, grid_cap, stream)
-                  : launch_d<Variant::Quad, 64>(mode, p, grid_cap, stream);
+  switch (var) {
+    case Variant::Whole: return launch_v<Variant::Whole>(D, mode, p, grid_cap, stream);
+    case Variant::Split: return launch_v<Variant::Split>(D, mode, p, grid_cap, stream);
+    case Variant::Masked: return launch_v<Variant::Masked>(D, mode, p, grid_cap, stream);
+  }
+  return -1;
 }
 
 }  // namespace fa

@@ -191,9 +191,10 @@ def test_ones_v_gives_ones():
 # ---------------------------------------------------------------- masks
 def test_full_mask_equals_dense():
     """A mask that keeps every tile gives the dense result.  Masked calls run
-    on the 4-wave kernel and dense ones on the 8-wave kernel (which splits the
-    keys of half-tiles), so the two sum in different orders: both must meet
-    the bound against the oracle, and the tag re-layout must be identical."""
+    on 128-query tiles with the keys split between two wave groups and dense
+    ones on 256-query tiles, so the two sum in different orders: both must
+    meet the bound against the oracle, and the tag re-layout must be
+    identical."""
     B, H, S, D, P = 1, 3, 1000, 128, 8
     qh, kh, vh = wl.random_qkv(B, H, S, D, seed=14)
     q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
@@ -216,7 +217,7 @@ def test_full_mask_equals_dense():
 @pytest.mark.parametrize("S,p_keep,B,D,scale", [
     (1000, 0.0, 1, 128, 0.088), (1000, 0.3, 1, 128, 0.088), (32760 // 4, 0.3, 1, 128, 0.088),
     (700, 0.7, 1, 128, 0.088), (1000, 0.5, 2, 64, 0.125), (777, 0.4, 3, 128, -0.09),
-    (129, 0.5, 2, 64, 0.2),
+    (129, 0.5, 2, 64, 0.2), (9000, 0.3, 1, 128, 0.088),
 ])
 def test_masked_parity(S, p_keep, B, D, scale):
     H, P = 3, 4 if S % 4 == 0 else 1
@@ -262,6 +263,34 @@ def test_fully_masked_rows_are_zero():
     assert np.all(out[0, 0, 128:256] == 0.0)
     ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0.1, words)
     assert_close(out, ref)
+
+
+def test_mask_stream_edges():
+    """Masked units split a row's kept stages between two wave groups.  Edge
+    rows at S = 300 (three mask tiles, the last holding 44 keys): only the
+    short last tile kept, so the second group's only stage has no key at all;
+    nothing kept; two tiles kept; every tile kept.  Bits for tiles past the
+    row's end are ignored (the same call with them set gives the same bits)."""
+    B, H, S, D, P = 1, 2, 300, 128, 3
+    q, k, v = wl.random_qkv(B, H, S, D, seed=19)
+    keep = np.zeros((H, 3, 3), dtype=bool)
+    keep[0, 0, 2] = True                 # one short tile: K = 1
+    keep[0, 2, [0, 2]] = True            # K = 2, its last stage empty
+    keep[1] = True                       # head 1: every tile
+    words = wl.pack_mask(keep)           # row 1 of head 0 keeps nothing
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    ref = oracle.attention(qd, kd, vd, 0.1, words)
+    absv = oracle.attention(qd, kd, np.abs(vd), 0.1, words)
+    qg, kg, vg = to_dev(q), to_dev(k), to_dev(v)
+    out = run_plain(qg, kg, vg, 0.1, mask_to_dev(words))
+    got = f64(out)
+    assert np.all(got[0, 0, 128:256] == 0.0)
+    assert_close(got, ref, "mask edges")
+    assert_within_bound(got, ref, absv, "mask edges")
+    junk = words.copy()
+    junk[..., 0] |= np.uint64(0xF0F0) << np.uint64(3)   # tiles 3 and up do not exist
+    out2 = run_plain(qg, kg, vg, 0.1, mask_to_dev(junk))
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
 # ------------------------------------------------------------ invariants
