@@ -348,6 +348,48 @@ def test_repeated_calls_bit_identical(case):
     torch.cuda.synchronize()
 
 
+def test_output_past_2_31_elements():
+    """Slab element offsets beyond 2^31 (64-bit store addressing, 64-bit head
+    offsets): 66560 heads of 256 tokens, integer-tagged so that every output
+    row is its own V row bit for bit.  The head index is spread over V's dims
+    3-5 (base 128, exact in bf16).  Rows sampled on both sides of the 2^31
+    boundary are compared with the tag values."""
+    import flashattention_output_re_amd as fa
+    B, H, S, D, P = 1, 66560, 256, 128, 2
+    Sp = S // P
+    assert B * H * S * D > 2 ** 31
+    say(f"[2^31] B={B} H={H} S={S} D={D} P={P}")
+    one = wl.tag_inputs(1, 1, S, D)
+    dev = torch.device("cuda:0")
+    q = one.q.to(dev).expand(B, H, S, D).contiguous()
+    v = one.v.to(dev).expand(B, H, S, D).contiguous()
+    hh = torch.arange(H, device=dev)
+    for col, val in ((3, 1 + hh % 128), (4, 1 + (hh // 128) % 128), (5, 1 + hh // 16384)):
+        v[0, :, :, col] = val[:, None].to(torch.bfloat16)
+    out = torch.full((P, B, Sp, H, D), -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    fa.attn_fwd_relayout_async(q, q, v, out, B, H, S, D, P, 1.0 / math.sqrt(D), None)
+    torch.cuda.synchronize()
+    del q, v
+    base = one.v[0, 0].view(torch.int16).numpy()
+    # Slab row index (p * Sp + t) * H + h; the first row past 2^31 elements and
+    # its neighbours, the last row, and rows far below.
+    r0 = 2 ** 31 // D
+    p0, rem = divmod(r0, Sp * H)
+    t0, h0 = divmod(rem, H)
+    where = [(0, 0, 0), (0, Sp - 1, H - 1), (1, 0, 0), (p0, t0, h0 - 1), (p0, t0, h0),
+             (p0, t0, h0 + 1), (p0, t0 + 1, 7), (P - 1, Sp - 1, H - 1)]
+    past = 0
+    for p, t, h in where:
+        got = out[p, 0, t, h].view(torch.int16).cpu().numpy()
+        want = base[p * Sp + t].copy()
+        want[3:6] = torch.tensor([1 + h % 128, 1 + (h // 128) % 128, 1 + h // 16384],
+                                 dtype=torch.bfloat16).view(torch.int16).numpy()
+        off = ((p * Sp + t) * H + h) * D
+        past += off >= 2 ** 31
+        assert np.array_equal(got, want), f"p={p} t={t} h={h}: element offset {off}"
+    assert past >= 4
+
+
 def test_blocking_entry_points():
     import flashattention_output_re_amd as fa
     B, H, S, D, P = 1, 2, 512, 64, 4
