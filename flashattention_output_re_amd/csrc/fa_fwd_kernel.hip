@@ -49,9 +49,8 @@ namespace fa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128;          // queries per output tile (= mask tile)
+constexpr int BM = 128;          // rows of a mask tile (queries and keys); masked unit size
 constexpr int BN = 64;           // keys per LDS stage
 constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
 // Tuning knob, overridable at build time (-D): operand reads issued ahead of
@@ -109,7 +108,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 template <int D> struct Tile {
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int ELEMS = BN * D;               // bf16 per stage
-  static constexpr int TOTAL = 4 * ELEMS;            // K and V, double buffered
 };
 // K rows are read 16 at a time at one logical chunk: XOR with the row's low bits.
 template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Tile<D>::CH - 1); }
