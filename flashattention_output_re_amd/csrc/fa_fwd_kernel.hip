@@ -434,16 +434,17 @@ __device__ __forceinline__ void store_tile(const FwdParams& p, const f32x16 (&ac
 // 2j + 2).  DMA is issued at the start of region S, into a slot whose last
 // readers finished before the barrier that opened the region (every wave of
 // a group reads all of a stage, so a slot may only be refilled once all of
-// them are past it), and waited for at the end of the wave's next region S,
-// before the barrier that precedes its readers.
+// them are past it), and waited for at the end of a later region S of the
+// same wave, before the barrier that precedes its readers.
 //
 // Whole units (SPLIT = false) are 256-query tiles: group 0 holds queries
 // [0, 128), group 1 queries [128, 256), and both read the same K/V stages, so
-// each stage crosses the L2 -> LDS path once per 256 queries.  Three buffers
-// per tensor: group 0 loads K stage n + 2 in S(n) into the slot of K stage
-// n - 1 (last read in phase 2n - 2), first read in phase 2n + 3; group 1 loads
-// V stage n + 2 in S(n) into the slot of V stage n - 1 (last read in phase
-// 2n), first read in phase 2n + 5.
+// each stage crosses the L2 -> LDS path once per 256 queries.  Four buffers
+// per tensor: group 0 loads K stage n + 3 in S(n) into the slot of K stage
+// n - 1 (last read in phase 2n - 2), first read in phase 2n + 5; group 1 loads
+// V stage n + 3 in S(n) into the slot of V stage n - 1 (last read in phase
+// 2n), first read in phase 2n + 7.  Each waits for a stage two S regions
+// after issuing it.
 //
 // Split units (SPLIT = true) fill the last, partial round of a launch: one
 // 128-query half of a 256-query tile, with the keys split between the groups
@@ -469,17 +470,22 @@ void fa_fwd_pp_kernel(FwdParams p) {
   constexpr int NB = 4 * NDB;     // PV MFMAs per stage
   constexpr int E = Tile<D>::ELEMS;
   constexpr int NG = SPLIT ? 2 : 1;          // K/V streams
-  constexpr int NBUF = SPLIT ? 2 : 3;        // buffers per tensor and stream
+  constexpr int NBUF = SPLIT ? 2 : 4;        // buffers per tensor and stream
   constexpr int PW = Dma<D>::PER_WAVE4;      // DMA instructions per wave, tensor and stage
-  constexpr int NDMA = SPLIT ? 2 * PW : PW;  // DMA instructions per wave and region S
+  // DMA instructions a wave may leave in flight at the end of region S: its
+  // last two regions' worth (whole units issue PW per region, split units
+  // 2 PW, and wait for the older of two regions or for the previous one).
+  constexpr int NDMA = 2 * PW;
   // Buffer [i][e] of stream i; one object per (tensor, slot) so that the
   // compiler can tell a DMA into one buffer from reads of another.
   __shared__ __attribute__((aligned(16))) uint16_t kb0[NG][E];
   __shared__ __attribute__((aligned(16))) uint16_t kb1[NG][E];
-  __shared__ __attribute__((aligned(16))) uint16_t kb2[NBUF == 3 ? NG : 1][NBUF == 3 ? E : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t kb2[NBUF >= 3 ? NG : 1][NBUF >= 3 ? E : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t kb3[NBUF == 4 ? NG : 1][NBUF == 4 ? E : 8];
   __shared__ __attribute__((aligned(16))) uint16_t vb0[NG][E];
   __shared__ __attribute__((aligned(16))) uint16_t vb1[NG][E];
-  __shared__ __attribute__((aligned(16))) uint16_t vb2[NBUF == 3 ? NG : 1][NBUF == 3 ? E : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vb2[NBUF >= 3 ? NG : 1][NBUF >= 3 ? E : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vb3[NBUF == 4 ? NG : 1][NBUF == 4 ? E : 8];
   // Group 1's running (max, sum) hand-over (split units only).
   __shared__ float ml[SPLIT ? 2 * 256 : 1];
 
@@ -502,19 +508,27 @@ void fa_fwd_pp_kernel(FwdParams p) {
   };
   // Stage j of the stream sits in kbuf(j % NBUF) / vbuf(j % NBUF).
   auto kbuf = [&](int slot) -> uint16_t* {
-    if (NBUF == 3 && slot == 2) return kb2[own];
+    if (NBUF >= 3 && slot == 2) return kb2[own];
+    if (NBUF == 4 && slot == 3) return kb3[own];
     return slot ? kb1[own] : kb0[own];
   };
   auto vbuf = [&](int slot) -> uint16_t* {
-    if (NBUF == 3 && slot == 2) return vb2[own];
+    if (NBUF >= 3 && slot == 2) return vb2[own];
+    if (NBUF == 4 && slot == 3) return vb3[own];
     return slot ? vb1[own] : vb0[own];
   };
   // Per-lane offsets of this wave's share of a K and of a V stage.
-  uint32_t koff[PW], voff[PW];
+  // Whole units: a wave only ever loads its group's tensor (group 0 K, group
+  // 1 V), so one set of offsets serves both calls below.
+  uint32_t koff[PW], voff[SPLIT ? PW : 1];
 #pragma unroll
   for (int q = 0; q < PW; ++q) {
-    koff[q] = dma_lane_off<D, false>(wq, lane, q);
-    voff[q] = dma_lane_off<D, true>(wq, lane, q);
+    if (SPLIT) {
+      koff[q] = dma_lane_off<D, false>(wq, lane, q);
+      voff[q] = dma_lane_off<D, true>(wq, lane, q);
+    } else {
+      koff[q] = grp == 0 ? dma_lane_off<D, false>(wq, lane, q) : dma_lane_off<D, true>(wq, lane, q);
+    }
   }
 
   // Dense units in XCD-aware order.  Masked units keep the plain order: on a
@@ -552,11 +566,11 @@ void fa_fwd_pp_kernel(FwdParams p) {
       dma_blocks<PW>(kbuf(slot) + 64 * 8 * PW * wq, rk, (uint32_t)key * (D * 2), koff);
     };
     auto dma_v = [&](int slot, int key) {
-      dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key * (D * 2), voff);
+      dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key * (D * 2), SPLIT ? voff : koff);
     };
     // The DMA issued at the start of region S(n) (SLOT = n % NBUF), after
     // the barrier that ends every wave's reads of the slots it refills.
-    // Whole units: K stage n + 2 (group 0) or V stage n + 2 (group 1) into
+    // Whole units: K stage n + 3 (group 0) or V stage n + 3 (group 1) into
     // the slot that stage n - 1 freed.  Split units, each group on its own
     // stream: K stage n + 2 into the slot of K stage n (read in M(n - 1)) and
     // V stage n + 1 into the slot of V stage n - 1 (read in M(n - 1)).
@@ -566,9 +580,9 @@ void fa_fwd_pp_kernel(FwdParams p) {
         dma_k(slot, MASKED ? key_n[2] : key_of(n + 2));
         dma_v((slot + 1) % NBUF, MASKED ? key_n[1] : key_of(n + 1));
       } else if (grp == 0) {
-        dma_k((slot + 2) % NBUF, key_of(n + 2));
+        dma_k((slot + 3) % NBUF, key_of(n + 3));
       } else {
-        dma_v((slot + 2) % NBUF, key_of(n + 2));
+        dma_v((slot + 3) % NBUF, key_of(n + 3));
       }
     };
 
@@ -591,17 +605,19 @@ void fa_fwd_pp_kernel(FwdParams p) {
     float l_run = 0.0f;
 
     // Prologue: K stages 0 and 1 and V stage 0 (SPLIT: each group, its own
-    // stream) or K stages 0, 1 (group 0) and V stages 0, 1 (group 1); every
+    // stream) or K stages 0-2 (group 0) and V stages 0-2 (group 1); every
     // wave computes the scores of its stream's first stage.
     if (SPLIT || grp == 0) {
       dma_k(0, stage_key(0));
       dma_k(1, stage_key(1));
     }
+    if (!SPLIT && grp == 0) dma_k(2, key_of(2));
     if (SPLIT) {
       dma_v(0, stage_key(0));
     } else if (grp == 1) {
       dma_v(0, stage_key(0));
       dma_v(1, stage_key(1));
+      dma_v(2, key_of(2));
     }
     wait_dma();
     __syncthreads();
@@ -611,7 +627,8 @@ void fa_fwd_pp_kernel(FwdParams p) {
     if (grp == 1) __syncthreads();   // group 1 starts one region behind
 
     // Region S(n), SLOT = n % NBUF: this wave's DMA, the softmax of stage n,
-    // then the wait for the DMA issued in S(n - 1).
+    // then the wait that completes this wave's DMA from S(n - 2) (split
+    // units: S(n - 1)) before the barrier that precedes its first readers.
     auto region_s = [&](auto SLOT, int n, StageProbs<NEG>& sm) {
       stage_dma(SLOT, n);
       mask_tail(s, MASKED ? key_n[0] : (own * nsh + n) * BN, p.S, g, fill);
@@ -677,9 +694,13 @@ void fa_fwd_pp_kernel(FwdParams p) {
       stage(std::integral_constant<int, 0>{}, n);
       if (n + 1 >= nloop) break;
       stage(std::integral_constant<int, 1>{}, n + 1);
-      if (NBUF == 3) {
+      if (NBUF >= 3) {
         if (n + 2 >= nloop) break;
         stage(std::integral_constant<int, 2 % NBUF>{}, n + 2);
+      }
+      if (NBUF == 4) {
+        if (n + 3 >= nloop) break;
+        stage(std::integral_constant<int, 3 % NBUF>{}, n + 3);
       }
     }
     wait_dma();   // DMA of stages past the end, before the buffers are reused
