@@ -291,7 +291,7 @@ def write_profile_report(workload: str, d: str):
     keep = wl.tile_mask_bool(w.H, w.S, w.keep_prob, w.seed) if w.keep_prob is not None else None
     flop = wl.flop_count(w.B, w.H, w.S, w.D, keep)
     stem = os.path.join(ROOT, "profiles", profile_prefix(workload))
-    short = (f"python bench.py --workload {workload} --steps 10 --warmup 2 --overhead-pairs 4 "
+    short = (f"python bench.py --workload {workload} --steps 30 --warmup 10 --overhead-pairs 4 "
              "--no-cpu-baseline --no-clock")
     sq1 = ("SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
            "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_MISC")
