@@ -348,6 +348,43 @@ def test_repeated_calls_bit_identical(case):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("case", ["dense, whole and split launches", "block mask"])
+def test_graph_capture_replays(case):
+    """A fused call allocates nothing and issues only kernel launches, so a
+    serving loop can record it in a HIP graph.  Each replay, with eager work
+    on the stream between replays, gives the eager result bit for bit."""
+    import flashattention_output_re_amd as fa
+    if case == "block mask":
+        B, H, S, D, P = 1, 3, 1000, 128, 4
+        keep = wl.tile_mask_bool(H, S, 0.4, seed=21)
+        mask = mask_to_dev(wl.pack_mask(keep))
+    else:
+        B, H, S, D, P = 1, _cus() + 5, 300, 128, 3
+        mask = None
+    say(f"[graph] {case}: B={B} H={H} S={S} D={D} P={P}")
+    q, k, v = (to_dev(t) for t in wl.random_qkv(B, H, S, D, seed=22))
+    scale = 1.0 / math.sqrt(D)
+    eager = torch.empty((P, B, S // P, H, D), dtype=torch.bfloat16, device=q.device)
+    fa.attn_fwd_relayout_async(q, k, v, eager, B, H, S, D, P, scale, mask)
+    out = torch.zeros_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.attn_fwd_relayout_async(q, k, v, out, B, H, S, D, P, scale, mask)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.attn_fwd_relayout_async(q, k, v, out, B, H, S, D, P, scale, mask)
+    for i in range(4):
+        out.fill_(0)
+        busy = (q.float() * 2.0).sum()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(busy)
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"{case}: replay {i}"
+
+
 def test_output_past_2_31_elements():
     """Slab element offsets beyond 2^31 (64-bit store addressing, 64-bit head
     offsets): 66560 heads of 256 tokens, integer-tagged so that every output
