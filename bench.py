@@ -312,7 +312,12 @@ def write_profile_report(workload: str, d: str):
 
     stats_f = glob.glob(os.path.join(d, f"trace_{workload}", "**", "*kernel_stats.csv"), recursive=True)[0]
     stats = {r["Name"]: r for r in csv.DictReader(open(stats_f))}
-    fused = sorted(n for n in stats if "fa_fwd" in n and "(fa::StoreMode)0" in n)
+    def flags(n):                  # template flags after StoreMode: NEG, SPLIT, MASKED, SLAB_IN
+        return [x.strip() for x in n.split("(fa::StoreMode)")[1].split(">")[0].split(",")[1:]]
+
+    fused = sorted(n for n in stats if "fa_fwd" in n and "(fa::StoreMode)0" in n
+                   and flags(n)[-1] == "false")
+    slab_in = sorted(n for n in stats if "fa_fwd" in n and flags(n)[-1] == "true")
     avg_s = {n: float(stats[n]["AverageNs"]) * 1e-9 for n in fused}
     call_s = sum(avg_s.values())
     bj = json.loads(open(os.path.join(d, f"bench_{workload}.json")).read().strip().splitlines()[-1])
@@ -350,6 +355,14 @@ def write_profile_report(workload: str, d: str):
           f"under the tracer; {flop:.4g} algorithmic FLOP per call -> {flop / call_s / 1e12:.1f} TFLOP/s "
           f"(bench.py, HIP events around the call: {bj['roofline']['mean_launch_ms']:.4f} ms, "
           f"{bj['roofline']['achieved']:.1f} TFLOP/s)."]
+    if slab_in and "slab_to_slab" in bj:
+        ms_in = [float(stats[n]["AverageNs"]) * 1e-6 for n in slab_in]
+        t_s = sum(ms_in) * 1e-3
+        tr.append(f"\nSlab-layout inputs (attn_fwd_slab_to_slab, last template flag true): "
+                  f"{' + '.join(f'{x:.4f}' for x in ms_in)} "
+                  f"= {t_s * 1e3:.4f} ms per call under the tracer, {flop / t_s / 1e12:.1f} TFLOP/s "
+                  f"(bench.py: {bj['slab_to_slab']['median_ms']:.4f} ms, "
+                  f"{bj['slab_to_slab']['overhead_vs_fused_pct']:+.2f}% against the fused call).")
     with open(f"{stem}_kernel_trace.md", "w") as f:
         f.write("\n".join(tr) + "\n")
 
@@ -541,6 +554,36 @@ def main():
     copy_ms = timed(copy, a.steps)
     copy_bytes = 2.0 * w.B * w.H * w.S * w.D * 2
 
+    # ---- both exchanges fused: Q, K, V arrive in the sequence-sharded slab
+    # layout (before the pre-attention exchange) and are read from there by
+    # the same kernel; alternated with the standard fused call.
+    Sp = w.S // w.P
+    qs, ks, vs = (t.view(w.B, w.H, w.P, Sp, w.D).permute(2, 0, 3, 1, 4).contiguous()
+                  for t in (q, k, v))
+    slabs3 = torch.empty_like(slabs)
+
+    def slab_in():
+        fa.attn_fwd_slab_to_slab_async(qs, ks, vs, slabs3, w.B, w.H, w.S, w.D, w.P, w.scale, mask,
+                                       stream)
+
+    for _ in range(2):
+        slab_in()
+    s2s, ref = [], []
+    for i in range(a.overhead_pairs):
+        order = (fused, slab_in) if i % 2 == 0 else (slab_in, fused)
+        for fn in order:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            (s2s if fn is slab_in else ref).append(e0.elapsed_time(e1))
+    med_s2s, med_ref = float(np.median(s2s)), float(np.median(ref))
+    sa, ra = np.array(s2s), np.array(ref)
+    boot2 = [np.median(rng.choice(sa, sa.size)) / np.median(rng.choice(ra, ra.size))
+             for _ in range(2000)]
+    del qs, ks, vs, slabs3
+
     achieved = flop / (mean_launch_ms * 1e-3) / 1e12
     traffic = load_traffic(a.workload)
     clk = {"sclk_mhz": None, "samples": 0, "error": "not sampled (--no-clock)"}
@@ -586,6 +629,14 @@ def main():
             "relayout_copy_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
             "relayout_copy_frac_of_8TBps": round(copy_bytes / (copy_ms * 1e-3) / 8e12, 4),
             "speedup_fused_over_serial": round(serial_ms / mean_launch_ms, 4),
+        },
+        "slab_to_slab": {
+            "what": "attn_fwd_slab_to_slab: q, k, v read from [P][B][S/P][H][D] slabs (the "
+                    "pre-attention exchange fused into the loads) and the output stored into slabs",
+            "median_ms": round(med_s2s, 4),
+            "TFLOPs": round(flop / (med_s2s * 1e-3) / 1e12, 2),
+            "overhead_vs_fused_pct": round((med_s2s / med_ref - 1.0) * 100.0, 2),
+            "overhead_ci95": [round(float((np.percentile(boot2, x) - 1) * 100), 2) for x in (2.5, 97.5)],
         },
     }
     if a.copy_calibration_mib:

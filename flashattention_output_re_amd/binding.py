@@ -33,6 +33,8 @@ _F = ctypes.c_float
 SIGNATURES = {
     "attn_fwd_relayout_async": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P],
     "attn_fwd_relayout": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
+    "attn_fwd_slab_to_slab_async": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P],
+    "attn_fwd_slab_to_slab": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_fwd_plain_async": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P],
     "attn_fwd_plain": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P],
     "relayout_to_slabs_async": [_P, _P, _I, _I, _I, _I, _I, _P],
@@ -140,6 +142,34 @@ def attn_fwd_relayout(q, k, v, out_slabs, B, H, S, D, P, scale, mask=None):
     st = load_library().attn_fwd_relayout(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out_slabs), B, H, S, D, P, float(scale), _ptr(mask))
     _raise(st, "attn_fwd_relayout")
+
+
+def attn_fwd_slab_to_slab_async(q_slabs, k_slabs, v_slabs, out_slabs, B, H, S, D, P, scale,
+                                mask=None, stream=None):
+    """Enqueue the whole Ulysses step: q, k, v and the output are all bf16
+    [P][B][S/P][H][D] (sequence-sharded slabs)."""
+    if P > 0 and S % P == 0:
+        for n, t in (("q_slabs", q_slabs), ("k_slabs", k_slabs), ("v_slabs", v_slabs),
+                     ("out_slabs", out_slabs)):
+            _check_tensor(n, t, (P, B, S // P, H, D))
+        _check_mask(mask, H, S)
+    st = load_library().attn_fwd_slab_to_slab_async(
+        _ptr(q_slabs), _ptr(k_slabs), _ptr(v_slabs), _ptr(out_slabs), B, H, S, D, P, float(scale),
+        _ptr(mask), _stream(stream))
+    _raise(st, "attn_fwd_slab_to_slab_async")
+
+
+def attn_fwd_slab_to_slab(q_slabs, k_slabs, v_slabs, out_slabs, B, H, S, D, P, scale, mask=None):
+    """Blocking variant on the null stream."""
+    if P > 0 and S % P == 0:
+        for n, t in (("q_slabs", q_slabs), ("k_slabs", k_slabs), ("v_slabs", v_slabs),
+                     ("out_slabs", out_slabs)):
+            _check_tensor(n, t, (P, B, S // P, H, D))
+        _check_mask(mask, H, S)
+    st = load_library().attn_fwd_slab_to_slab(
+        _ptr(q_slabs), _ptr(k_slabs), _ptr(v_slabs), _ptr(out_slabs), B, H, S, D, P, float(scale),
+        _ptr(mask))
+    _raise(st, "attn_fwd_slab_to_slab")
 
 
 def attn_fwd_plain_async(q, k, v, out, B, H, S, D, scale, mask=None, stream=None):

@@ -69,9 +69,31 @@ int grid_cap_for(int D, fa::StoreMode mode, fa::Variant var) {
   return gm.cus * occ;
 }
 
+// Extra checks for slab-layout inputs: a stage of 64 keys may cross at most
+// one slab boundary, and a whole input tensor is addressed with 32-bit byte
+// offsets.
+int validate_slab_in(int B, int H, int S, int D, int P) {
+  if (S / P < 64) return FA_EUNSUPPORTED;
+  if ((int64_t)B * H * S * D * 2 > (int64_t)INT32_MAX) return FA_ERANGE;
+  return FA_OK;
+}
+
+// Constants for n / d with (umulhi(n, magic) + n) >> shift, exact for
+// n < 2^31 and 1 <= d < 2^31 (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994): shift = ceil(log2 d),
+// magic = floor(2^32 (2^shift - d) / d) + 1.
+void div_magic(uint32_t d, uint32_t* magic, int* shift) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  *shift = l;
+  *magic = (uint32_t)((((uint64_t)1 << 32) * ((1ull << l) - d)) / d + 1);
+}
+
 int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* out, int B, int H,
-        int S, int D, int P, float scale, const uint64_t* mask, hipStream_t stream) {
-  const int st = validate(q, k, v, out, B, H, S, D, P, scale, mask);
+        int S, int D, int P, float scale, const uint64_t* mask, hipStream_t stream,
+        bool slab_in = false) {
+  int st = validate(q, k, v, out, B, H, S, D, P, scale, mask);
+  if (st == FA_OK && slab_in) st = validate_slab_in(B, H, S, D, P);
   if (st != FA_OK) return st;
   // Dense attention runs on 256-query tiles; a block mask gives each
   // 128-query tile its own key set, so masked calls run on 128-query tiles
@@ -90,6 +112,7 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   p.S = S;
   p.P = P;
   p.Sp = S / P;
+  div_magic((uint32_t)p.Sp, &p.sp_magic, &p.sp_shift);
   const int rows = fa::tile_rows(var);
   p.nqt = (S + rows - 1) / rows;
   p.units = B * H * p.nqt;
@@ -102,7 +125,7 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   // and keeps (-inf) * c = -inf for the keys past S.
   if (p.c == 0.0f) p.c = 1e-30f;
   if (mask)
-    return fa::launch_fwd(D, mode, var, p, cap, stream) == 0 ? FA_OK : FA_ELAUNCH;
+    return fa::launch_fwd(D, mode, var, p, cap, stream, slab_in) == 0 ? FA_OK : FA_ELAUNCH;
 
   // Dense: whole 256-query tiles fill `cap` CUs per round.  When the last
   // round would keep at most half of the CUs busy, its R tiles run instead as
@@ -111,16 +134,17 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   const int tail = p.units % cap;
   const int stages = (S + 63) / 64;
   if (tail == 0 || 2 * tail > cap || stages < 2)
-    return fa::launch_fwd(D, mode, var, p, cap, stream) == 0 ? FA_OK : FA_ELAUNCH;
+    return fa::launch_fwd(D, mode, var, p, cap, stream, slab_in) == 0 ? FA_OK : FA_ELAUNCH;
   const int split_cap = grid_cap_for(D, mode, fa::Variant::Split);
   if (split_cap <= 0) return FA_EDEVICE;
   fa::FwdParams whole = p;
   whole.units = p.units - tail;
-  if (whole.units > 0 && fa::launch_fwd(D, mode, var, whole, cap, stream) != 0) return FA_ELAUNCH;
+  if (whole.units > 0 && fa::launch_fwd(D, mode, var, whole, cap, stream, slab_in) != 0)
+    return FA_ELAUNCH;
   fa::FwdParams half = p;
   half.units = 2 * tail;
   half.unit_base = p.units - tail;
-  return fa::launch_fwd(D, mode, fa::Variant::Split, half, split_cap, stream) == 0
+  return fa::launch_fwd(D, mode, fa::Variant::Split, half, split_cap, stream, slab_in) == 0
              ? FA_OK : FA_ELAUNCH;
 }
 
@@ -180,6 +204,20 @@ int attn_fwd_relayout(const void* q, const void* k, const void* v, void* out_sla
       run(fa::StoreMode::Slab, q, k, v, out_slabs, B, H, S, D, P, scale, mask, nullptr));
 }
 
+int attn_fwd_slab_to_slab_async(const void* q_slabs, const void* k_slabs, const void* v_slabs,
+                                void* out_slabs, int B, int H, int S, int D, int P, float scale,
+                                const uint64_t* mask, void* stream) {
+  return run(fa::StoreMode::Slab, q_slabs, k_slabs, v_slabs, out_slabs, B, H, S, D, P, scale,
+             mask, static_cast<hipStream_t>(stream), true);
+}
+
+int attn_fwd_slab_to_slab(const void* q_slabs, const void* k_slabs, const void* v_slabs,
+                          void* out_slabs, int B, int H, int S, int D, int P, float scale,
+                          const uint64_t* mask) {
+  return finish_blocking(run(fa::StoreMode::Slab, q_slabs, k_slabs, v_slabs, out_slabs, B, H, S,
+                             D, P, scale, mask, nullptr, true));
+}
+
 int attn_fwd_plain_async(const void* q, const void* k, const void* v, void* out, int B, int H,
                          int S, int D, float scale, const uint64_t* mask, void* stream) {
   return run(fa::StoreMode::Plain, q, k, v, out, B, H, S, D, 1, scale, mask,
@@ -206,7 +244,8 @@ const char* attn_status_string(int status) {
     case FA_OK: return "ok";
     case FA_EINVAL: return "invalid argument (null tensor, non-positive size or non-finite scale)";
     case FA_EDIV: return "S is not a multiple of the slab count P";
-    case FA_EUNSUPPORTED: return "unsupported head dimension (D must be 64 or 128)";
+    case FA_EUNSUPPORTED:
+      return "unsupported shape (D must be 64 or 128; slab inputs need S/P >= 64)";
     case FA_EALIGN: return "misaligned pointer (tensors need 16 bytes, the mask 8)";
     case FA_ERANGE: return "sizes exceed the kernel's index range";
     case FA_ELAUNCH: return "kernel launch failed";

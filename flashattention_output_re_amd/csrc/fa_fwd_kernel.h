@@ -31,11 +31,17 @@ struct FwdParams {
   int nmt;               // 128-key mask tiles per row (= nqt)
   int mw;                // 64-bit words per mask row
   float c;               // scale * log2(e)
+  // Slab-layout inputs only: n / Sp = (umulhi(n, sp_magic) + n) >> sp_shift
+  // for n < 2^31.
+  uint32_t sp_magic;
+  int sp_shift;
 };
 
 // Launch with at most `grid_cap` persistent workgroups; 0 on success.
+// slab_in: q, k, v are [P][B][S/P][H][D] (sequence-sharded) instead of
+// [B][H][S][D]; only with StoreMode::Slab.
 int launch_fwd(int D, StoreMode mode, Variant var, const FwdParams& p, int grid_cap,
-               hipStream_t stream);
+               hipStream_t stream, bool slab_in = false);
 // Resident workgroups per CU for the instance (D, mode, var); 0 on success.
 int kernel_occupancy(int D, StoreMode mode, Variant var, int* blocks_per_cu);
 

@@ -459,7 +459,7 @@ __device__ __forceinline__ void store_tile(const FwdParams& p, const f32x16 (&ac
 // mask: the row's K kept 128-key tiles give 2K stages in key order, group 0
 // takes the first K and group 1 the rest (KeptStages), with the split
 // schedule above; tiles the mask drops are never loaded.
-template <int D, StoreMode MODE, bool NEG, bool SPLIT, bool MASKED = false>
+template <int D, StoreMode MODE, bool NEG, bool SPLIT, bool MASKED = false, bool SLAB_IN = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_pp_kernel(FwdParams p) {
@@ -530,6 +530,21 @@ void fa_fwd_pp_kernel(FwdParams p) {
       koff[q] = grp == 0 ? dma_lane_off<D, false>(wq, lane, q) : dma_lane_off<D, true>(wq, lane, q);
     }
   }
+  // Slab-layout inputs: key rows of one (b, h) are H D 2 bytes apart within a
+  // slab, so a lane's offset within a stage becomes row * rowstride + chunk.
+  // row0 is the lane's row in its first DMA instruction; instruction q moves
+  // rows row0 + q * (64 / CH).
+  constexpr int SH = D == 128 ? 8 : 7;                 // log2(D * 2)
+  const uint32_t rowstride = (uint32_t)p.H * D * 2;
+  const uint32_t in_bytes = (uint32_t)p.B * p.H * p.S * D * 2;
+  const int row0 = (int)(koff[0] >> SH);
+  if (SLAB_IN) {
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+      koff[q] = (koff[q] >> SH) * rowstride + (koff[q] & (2 * D - 1));
+      if (SPLIT) voff[q] = (voff[q] >> SH) * rowstride + (voff[q] & (2 * D - 1));
+    }
+  }
 
   // Dense units in XCD-aware order.  Masked units keep the plain order: on a
   // 30%-dense block mask the XCD-aware order measured slower (its workgroups
@@ -543,10 +558,42 @@ void fa_fwd_pp_kernel(FwdParams p) {
     const int tile = MASKED ? unit : SPLIT ? p.unit_base + (unit >> 1) : unit;
     const int bh = tile / p.nqt, qt = tile - bh * p.nqt;
     const int b = bh / p.H, h = bh - b * p.H;
-    const size_t head_off = (size_t)bh * p.S * D;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_off, head_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, head_bytes);
+    // [B][H][S][D] inputs: one resource per head slice.  Slab inputs: one per
+    // tensor, with the head's columns at head_col of every row.
+    const size_t head_off = SLAB_IN ? 0 : (size_t)bh * p.S * D;
+    const uint32_t in_size = SLAB_IN ? in_bytes : head_bytes;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_off, in_size);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, in_size);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, in_size);
+    const uint32_t head_col = (uint32_t)h * D * 2;
+    // Slab inputs: byte offset of the row of token s < S of this (b, h).
+    auto slab_row = [&](uint32_t s) {
+      const uint32_t ps = (__umulhi(s, p.sp_magic) + s) >> p.sp_shift;
+      return ((ps * p.B + b) * p.Sp + (s - ps * p.Sp)) * rowstride + head_col;
+    };
+    // Slab inputs: this wave's share of the stage that starts at key `key`
+    // into `dst`, lane offsets `lo` within the stage's first slab.  A stage
+    // that runs past the end of a slab continues in the next slab, (B - 1) Sp
+    // rows further on (Sp >= 64, so at most one boundary); keys >= S land
+    // past the tensor and read as zeros.
+    auto slab_dma = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo, int key) {
+      if (key >= p.S) {
+        dma_blocks<PW>(dst, r, in_bytes, lo);
+        return;
+      }
+      const uint32_t ps = (__umulhi((uint32_t)key, p.sp_magic) + key) >> p.sp_shift;
+      const uint32_t base = ((ps * p.B + b) * p.Sp + (key - ps * p.Sp)) * rowstride + head_col;
+      const int left = (int)((ps + 1) * p.Sp) - key;    // rows before the boundary
+      if (left >= BN) {
+        dma_blocks<PW>(dst, r, base, lo);
+        return;
+      }
+      const uint32_t delta = (uint32_t)(p.B - 1) * p.Sp * rowstride;
+      uint32_t o[PW];
+#pragma unroll
+      for (int q = 0; q < PW; ++q) o[q] = lo[q] + (row0 + q * (64 / Tile<D>::CH) >= left ? delta : 0u);
+      dma_blocks<PW>(dst, r, base, o);
+    };
     // Masked units: this group's stream of kept stages, and the first keys of
     // stages n, n + 1 and n + 2 of the stream (key_n[0..2]), advanced after
     // each stage.
@@ -563,10 +610,18 @@ void fa_fwd_pp_kernel(FwdParams p) {
     auto stage_key = [&](int j) { return MASKED ? key_n[j] : key_of(j); };
     // This wave's share of the K or V stage that starts at key `key` into slot `slot`.
     auto dma_k = [&](int slot, int key) {
-      dma_blocks<PW>(kbuf(slot) + 64 * 8 * PW * wq, rk, (uint32_t)key * (D * 2), koff);
+      if constexpr (SLAB_IN) {
+        slab_dma(kbuf(slot) + 64 * 8 * PW * wq, rk, koff, key);
+      } else {
+        dma_blocks<PW>(kbuf(slot) + 64 * 8 * PW * wq, rk, (uint32_t)key * (D * 2), koff);
+      }
     };
     auto dma_v = [&](int slot, int key) {
-      dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key * (D * 2), SPLIT ? voff : koff);
+      if constexpr (SLAB_IN) {
+        slab_dma(vbuf(slot) + 64 * 8 * PW * wq, rv, SPLIT ? voff : koff, key);
+      } else {
+        dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key * (D * 2), SPLIT ? voff : koff);
+      }
     };
     // The DMA issued at the start of region S(n) (SLOT = n % NBUF), after
     // the barrier that ends every wave's reads of the slots it refills.
@@ -589,10 +644,12 @@ void fa_fwd_pp_kernel(FwdParams p) {
     const int qrow = MASKED  ? qt * BM + wq * 32 + l32
                      : SPLIT ? qt * 256 + (unit & 1) * 128 + wq * 32 + l32
                              : qt * 256 + wave * 32 + l32;
+    const uint32_t qbase = !SLAB_IN ? (uint32_t)(qrow * D * 2)
+                           : qrow < p.S ? slab_row((uint32_t)qrow) : in_bytes;
     bf16x8 qf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, load16(rq, (uint32_t)(qrow * D * 2 + ks * 32 + g * 16)));
+      qf[ks] = __builtin_bit_cast(bf16x8, load16(rq, qbase + ks * 32 + g * 16));
 
     f32x16 acc[NDB];
 #pragma unroll
@@ -751,11 +808,11 @@ void fa_fwd_pp_kernel(FwdParams p) {
 template <Variant VAR> constexpr bool kSplit = VAR != Variant::Whole;
 template <Variant VAR> constexpr bool kMasked = VAR == Variant::Masked;
 
-template <Variant VAR, int D, StoreMode MODE, bool NEG>
+template <Variant VAR, int D, StoreMode MODE, bool NEG, bool SLAB_IN>
 static int launch_one(const FwdParams& p, int grid_cap, hipStream_t stream) {
   const int grid = p.units < grid_cap ? p.units : grid_cap;
-  hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, kSplit<VAR>, kMasked<VAR>>), dim3(grid),
-                     dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, kSplit<VAR>, kMasked<VAR>, SLAB_IN>),
+                     dim3(grid), dim3(512), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -789,31 +846,37 @@ int kernel_occupancy(int D, StoreMode mode, Variant var, int* blocks_per_cu) {
   return -1;
 }
 
-template <Variant VAR, int D, StoreMode MODE>
+template <Variant VAR, int D, StoreMode MODE, bool SLAB_IN>
 static int launch_sign(const FwdParams& p, int grid_cap, hipStream_t stream) {
-  return p.c < 0.0f ? launch_one<VAR, D, MODE, true>(p, grid_cap, stream)
-                    : launch_one<VAR, D, MODE, false>(p, grid_cap, stream);
+  return p.c < 0.0f ? launch_one<VAR, D, MODE, true, SLAB_IN>(p, grid_cap, stream)
+                    : launch_one<VAR, D, MODE, false, SLAB_IN>(p, grid_cap, stream);
 }
 
+// Slab-layout inputs are instantiated with slab outputs only.
 template <Variant VAR, int D>
-static int launch_d(StoreMode mode, const FwdParams& p, int grid_cap, hipStream_t stream) {
-  return mode == StoreMode::Slab ? launch_sign<VAR, D, StoreMode::Slab>(p, grid_cap, stream)
-                                 : launch_sign<VAR, D, StoreMode::Plain>(p, grid_cap, stream);
+static int launch_d(StoreMode mode, const FwdParams& p, int grid_cap, hipStream_t stream,
+                    bool slab_in) {
+  if (slab_in)
+    return mode == StoreMode::Slab ? launch_sign<VAR, D, StoreMode::Slab, true>(p, grid_cap, stream)
+                                   : -1;
+  return mode == StoreMode::Slab ? launch_sign<VAR, D, StoreMode::Slab, false>(p, grid_cap, stream)
+                                 : launch_sign<VAR, D, StoreMode::Plain, false>(p, grid_cap, stream);
 }
 
 template <Variant VAR>
-static int launch_v(int D, StoreMode mode, const FwdParams& p, int grid_cap, hipStream_t stream) {
-  return D == 128 ? launch_d<VAR, 128>(mode, p, grid_cap, stream)
-                  : launch_d<VAR, 64>(mode, p, grid_cap, stream);
+static int launch_v(int D, StoreMode mode, const FwdParams& p, int grid_cap, hipStream_t stream,
+                    bool slab_in) {
+  return D == 128 ? launch_d<VAR, 128>(mode, p, grid_cap, stream, slab_in)
+                  : launch_d<VAR, 64>(mode, p, grid_cap, stream, slab_in);
 }
 
 int launch_fwd(int D, StoreMode mode, Variant var, const FwdParams& p, int grid_cap,
-               hipStream_t stream) {
+               hipStream_t stream, bool slab_in) {
   if (D != 64 && D != 128) return -1;
   switch (var) {
-    case Variant::Whole: return launch_v<Variant::Whole>(D, mode, p, grid_cap, stream);
-    case Variant::Split: return launch_v<Variant::Split>(D, mode, p, grid_cap, stream);
-    case Variant::Masked: return launch_v<Variant::Masked>(D, mode, p, grid_cap, stream);
+    case Variant::Whole: return launch_v<Variant::Whole>(D, mode, p, grid_cap, stream, slab_in);
+    case Variant::Split: return launch_v<Variant::Split>(D, mode, p, grid_cap, stream, slab_in);
+    case Variant::Masked: return launch_v<Variant::Masked>(D, mode, p, grid_cap, stream, slab_in);
   }
   return -1;
 }

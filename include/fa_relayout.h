@@ -58,7 +58,7 @@ extern "C" {
 #define FA_OK 0
 #define FA_EINVAL (-1)        /* null q/k/v/out; B, H, S or P <= 0; scale not finite */
 #define FA_EDIV (-2)          /* S is not a multiple of P */
-#define FA_EUNSUPPORTED (-3)  /* D is not 64 or 128 */
+#define FA_EUNSUPPORTED (-3)  /* D is not 64 or 128 (slab inputs: S/P < 64) */
 #define FA_EALIGN (-4)        /* a tensor pointer not 16-byte aligned, mask not 8 */
 #define FA_ERANGE (-5)        /* (S+256)*D*2 bytes per head >= 2^31, or too many tiles */
 #define FA_ELAUNCH (-6)       /* the kernel launch was rejected */
@@ -78,6 +78,28 @@ int attn_fwd_relayout_async(const void* q, const void* k, const void* v,
 int attn_fwd_relayout(const void* q, const void* k, const void* v,
                       void* out_slabs, int B, int H, int S, int D, int P,
                       float scale, const uint64_t* mask);
+
+/* The whole Ulysses attention step on one GPU: both exchanges fused into the
+ * attention kernel.  Ulysses sequence parallelism (named in the X-Stage
+ * abstract, CatalyzeX and fugumt pages) exchanges twice around attention:
+ * sequence -> head before it, head -> sequence after it.  The pages describe
+ * fusing the second into FlashAttention; this entry point also fuses the
+ * first into the Q/K/V loads (an extension the pages do not describe): the
+ * inputs arrive sequence-sharded, q_slabs[p][b][t][h][d] = Q[b][h][p*(S/P) +
+ * t][d] (the layout of out_slabs), and each tile's owner reads its head's
+ * rows straight from the P slabs.  The result equals attn_fwd_relayout on the
+ * same Q, K, V in [B][H][S][D] bit for bit.
+ * q_slabs, k_slabs, v_slabs, out_slabs: bf16 [P][B][S/P][H][D], contiguous,
+ * 16-byte aligned; outputs must not overlap inputs.  Same validation and
+ * status codes as attn_fwd_relayout, plus FA_EUNSUPPORTED when S/P < 64 and
+ * FA_ERANGE when one input tensor holds 2^31 bytes or more. */
+int attn_fwd_slab_to_slab_async(const void* q_slabs, const void* k_slabs, const void* v_slabs,
+                                void* out_slabs, int B, int H, int S, int D, int P, float scale,
+                                const uint64_t* mask, void* stream);
+
+int attn_fwd_slab_to_slab(const void* q_slabs, const void* k_slabs, const void* v_slabs,
+                          void* out_slabs, int B, int H, int S, int D, int P, float scale,
+                          const uint64_t* mask);
 
 /* The same attention kernel writing the plain layout out[b][h][s][d]
  * (bf16 [B][H][S][D]) instead of the slabs: the measurement twin that the

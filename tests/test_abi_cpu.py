@@ -99,6 +99,23 @@ def test_plain_validation(lib, kw, code):
     assert _plain(lib, **kw) == code
 
 
+def _s2s(lib, q=A, k=B_, v=C, out=O, Bn=1, H=2, S=256, D=128, P=2, scale=0.1, mask=None):
+    return lib.attn_fwd_slab_to_slab_async(q, k, v, out, Bn, H, S, D, P, scale, mask, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(v=None), -1), (dict(out=None), -1), (dict(Bn=0), -1),
+    (dict(scale=math.nan), -1), (dict(S=255, P=2), -2), (dict(D=96), -3),
+    (dict(S=256, P=8), -3),            # 32 tokens per slab: a 64-key stage could span three slabs
+    (dict(S=126, P=2), -3),
+    (dict(k=B_ + 8), -4), (dict(mask=M + 4), -4),
+    (dict(Bn=1, H=1 << 10, S=1 << 13, D=128, P=2), -5),     # 2^31 bytes per input tensor
+    (dict(S=(1 << 23), D=128, P=1), -5),
+])
+def test_slab_to_slab_validation(lib, kw, code):
+    assert _s2s(lib, **kw) == code
+
+
 def _copy(lib, plain=A, out=O, Bn=1, H=2, S=256, D=128, P=2):
     return lib.relayout_to_slabs_async(plain, out, Bn, H, S, D, P, None)
 
@@ -119,6 +136,7 @@ def test_blocking_entry_points_validate(lib):
     assert lib.attn_fwd_plain(A, B_, C, O, 1, 1, 256, 48, 0.1, None) == -3
     assert lib.relayout_to_slabs(None, O, 1, 1, 256, 128, 2) == -1
     assert lib.relayout_to_slabs(A, O, 1, 1, 256, 128, 3) == -2
+    assert lib.attn_fwd_slab_to_slab(A, B_, C, O, 1, 1, 256, 128, 8, 0.1, None) == -3
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
@@ -126,6 +144,7 @@ def test_valid_arguments_without_device_report_no_device(lib):
     assert _relayout(lib) == -7
     assert _plain(lib) == -7
     assert _copy(lib) == -7
+    assert _s2s(lib) == -7
 
 
 def test_python_binding_raises(lib):
