@@ -459,6 +459,12 @@ __device__ __forceinline__ void store_tile(const FwdParams& p, const f32x16 (&ac
 // mask: the row's K kept 128-key tiles give 2K stages in key order, group 0
 // takes the first K and group 1 the rest (KeptStages), with the split
 // schedule above; tiles the mask drops are never loaded.
+//
+// SLAB_IN (any form, slab output only): q, k and v arrive sequence-sharded,
+// [P][B][S/P][H][D], as before Ulysses' pre-attention exchange, and the loads
+// read the tile's head straight from the slabs (slab_row, slab_dma); the
+// arithmetic is unchanged, so the result equals that of [B][H][S][D] inputs
+// bit for bit.
 template <int D, StoreMode MODE, bool NEG, bool SPLIT, bool MASKED = false, bool SLAB_IN = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
                           amdgpu_waves_per_eu(2, 2)))
@@ -536,7 +542,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
   // rows row0 + q * (64 / CH).
   constexpr int SH = D == 128 ? 8 : 7;                 // log2(D * 2)
   const uint32_t rowstride = (uint32_t)p.H * D * 2;
-  const uint32_t in_bytes = (uint32_t)p.B * p.H * p.S * D * 2;
+  const uint32_t in_bytes = (uint32_t)p.B * p.H * p.S * D * 2;   // < 2^31 for slab inputs
   const int row0 = (int)(koff[0] >> SH);
   if (SLAB_IN) {
 #pragma unroll
