@@ -168,7 +168,29 @@ __device__ __forceinline__ void dma_blocks(uint16_t* dst, __amdgpu_buffer_rsrc_t
         : "memory", "m0");
   }
 }
+// One such instruction on its own: 16 bytes per lane from byte offset `addr`
+// of r into LDS byte address lds + 16 lane.
+__device__ __forceinline__ void dma_one(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(addr), "s"(r)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// A wave's share of one K or V stage as N single instructions that can be
+// issued apart: instruction i moves the 1 KB block at LDS byte address
+// lds + 1024 i from the lane offsets addr[i].
+template <int N>
+struct DmaPlan {
+  uint32_t lds;
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t addr[N];
+  __device__ __forceinline__ void issue(int i) const { dma_one(lds + 1024u * i, r, addr[i]); }
+};
 
 // Byte offset, from the stage's first key, that lane `lane` of wave `wave`
 // (of four) reads in DMA instruction q of a K (SWZ_V = false) or V stage.
@@ -326,7 +348,21 @@ struct StageProbs {
   bool rescale = false;
   uint32_t pk[16];
 
-  __device__ __forceinline__ void compute(f32x16 (&sc)[2], float c, float& m_run, float& l_run) {
+  // With SPREAD, issue(j), j = 0..3, issues this wave's share of the
+  // region's LDS DMA at four points spread over the VALU work, so that the
+  // waves of a group do not all queue their DMA instructions at the region's
+  // start (split-key units, which move two stages per region).
+  template <bool SPREAD, class Issue>
+  __device__ __forceinline__ void compute(f32x16 (&sc)[2], float c, float& m_run, float& l_run,
+                                          const Issue& issue) {
+    auto point = [&](int j) {
+      if constexpr (SPREAD) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    point(0);
     float e[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -345,10 +381,13 @@ struct StageProbs {
     alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_use;
     const float neg_m = -m_use;
+    point(1);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[mb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r], c, neg_m));
+      point(2 + mb);
+    }
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -431,7 +470,7 @@ __device__ __forceinline__ void store_tile(const FwdParams& p, const f32x16 (&ac
 // Phases t are separated by barriers: group 0 runs S(n) in t = 2n and M(n) in
 // 2n + 1, group 1 runs S(n) in 2n + 1 and M(n) in 2n + 2.  K stage j is read in
 // M(j - 1) (phases 2j - 1 and 2j), V stage j in M(j) (phases 2j + 1 and
-// 2j + 2).  DMA is issued at the start of region S, into a slot whose last
+// 2j + 2).  DMA is issued in region S, into a slot whose last
 // readers finished before the barrier that opened the region (every wave of
 // a group reads all of a stage, so a slot may only be refilled once all of
 // them are past it), and waited for at the end of a later region S of the
@@ -600,6 +639,32 @@ void fa_fwd_pp_kernel(FwdParams p) {
       for (int q = 0; q < PW; ++q) o[q] = lo[q] + (row0 + q * (64 / Tile<D>::CH) >= left ? delta : 0u);
       dma_blocks<PW>(dst, r, base, o);
     };
+    // The same share as a DmaPlan (any input layout): the byte offsets of
+    // instruction q are those dma_blocks / slab_dma would use.
+    auto plan_of = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo, int key) {
+      DmaPlan<PW> pl;
+      pl.lds = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
+      pl.r = r;
+      if constexpr (SLAB_IN) {
+        if (key >= p.S) {
+#pragma unroll
+          for (int q = 0; q < PW; ++q) pl.addr[q] = in_bytes + lo[q];
+        } else {
+          const uint32_t ps = (__umulhi((uint32_t)key, p.sp_magic) + key) >> p.sp_shift;
+          const uint32_t base = ((ps * p.B + b) * p.Sp + (key - ps * p.Sp)) * rowstride + head_col;
+          const int left = (int)((ps + 1) * p.Sp) - key;
+          const uint32_t delta = (uint32_t)(p.B - 1) * p.Sp * rowstride;
+#pragma unroll
+          for (int q = 0; q < PW; ++q)
+            pl.addr[q] = base + lo[q] + (row0 + q * (64 / Tile<D>::CH) >= left ? delta : 0u);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < PW; ++q) pl.addr[q] = (uint32_t)key * (D * 2) + lo[q];
+      }
+      return pl;
+    };
     // Masked units: this group's stream of kept stages, and the first keys of
     // stages n, n + 1 and n + 2 of the stream (key_n[0..2]), advanced after
     // each stage.
@@ -629,22 +694,28 @@ void fa_fwd_pp_kernel(FwdParams p) {
         dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key * (D * 2), SPLIT ? voff : koff);
       }
     };
-    // The DMA issued at the start of region S(n) (SLOT = n % NBUF), after
-    // the barrier that ends every wave's reads of the slots it refills.
+    // The DMA issued in region S(n) (SLOT = n % NBUF), after the barrier
+    // that ends every wave's reads of the slots it refills: whole units at
+    // the region's start, split units at four points of its softmax.
     // Whole units: K stage n + 3 (group 0) or V stage n + 3 (group 1) into
     // the slot that stage n - 1 freed.  Split units, each group on its own
     // stream: K stage n + 2 into the slot of K stage n (read in M(n - 1)) and
     // V stage n + 1 into the slot of V stage n - 1 (read in M(n - 1)).
     auto stage_dma = [&](auto SLOT, int n) {
       constexpr int slot = decltype(SLOT)::value;
-      if (SPLIT) {
-        dma_k(slot, MASKED ? key_n[2] : key_of(n + 2));
-        dma_v((slot + 1) % NBUF, MASKED ? key_n[1] : key_of(n + 1));
-      } else if (grp == 0) {
+      if (grp == 0) {
         dma_k((slot + 3) % NBUF, key_of(n + 3));
       } else {
         dma_v((slot + 3) % NBUF, key_of(n + 3));
       }
+    };
+    // Split units: the same stages as DmaPlans, issued during the softmax.
+    struct SplitPlans { DmaPlan<PW> k, v; };
+    auto split_plans = [&](auto SLOT, int n) {
+      constexpr int slot = decltype(SLOT)::value;
+      const int wofs = 64 * 8 * PW * wq;
+      return SplitPlans{plan_of(kbuf(slot) + wofs, rk, koff, MASKED ? key_n[2] : key_of(n + 2)),
+                        plan_of(vbuf((slot + 1) % NBUF) + wofs, rv, voff, MASKED ? key_n[1] : key_of(n + 1))};
     };
 
     const int qrow = MASKED  ? qt * BM + wq * 32 + l32
@@ -693,9 +764,22 @@ void fa_fwd_pp_kernel(FwdParams p) {
     // then the wait that completes this wave's DMA from S(n - 2) (split
     // units: S(n - 1)) before the barrier that precedes its first readers.
     auto region_s = [&](auto SLOT, int n, StageProbs<NEG>& sm) {
-      stage_dma(SLOT, n);
-      mask_tail(s, MASKED ? key_n[0] : (own * nsh + n) * BN, p.S, g, fill);
-      sm.compute(s, c, m_run, l_run);
+      const int key0 = MASKED ? key_n[0] : (own * nsh + n) * BN;
+      if constexpr (SPLIT) {
+        const SplitPlans pl = split_plans(SLOT, n);
+        mask_tail(s, key0, p.S, g, fill);
+        sm.template compute<true>(s, c, m_run, l_run, [&](int j) {
+          constexpr int STEP = 4 / PW;
+          if (j % STEP == 0) {
+            pl.k.issue(j / STEP);
+            pl.v.issue(j / STEP);
+          }
+        });
+      } else {
+        stage_dma(SLOT, n);
+        mask_tail(s, key0, p.S, g, fill);
+        sm.template compute<false>(s, c, m_run, l_run, [](int) {});
+      }
       wait_vm<NDMA>();
     };
     // Region M(n): the scores of stage n + 1 (K stage n + 1) and PV of stage
