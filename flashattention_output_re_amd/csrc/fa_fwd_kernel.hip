@@ -639,30 +639,15 @@ void fa_fwd_pp_kernel(FwdParams p) {
       for (int q = 0; q < PW; ++q) o[q] = lo[q] + (row0 + q * (64 / Tile<D>::CH) >= left ? delta : 0u);
       dma_blocks<PW>(dst, r, base, o);
     };
-    // The same share as a DmaPlan (any input layout): the byte offsets of
-    // instruction q are those dma_blocks / slab_dma would use.
+    // The same share as a DmaPlan ([B][H][S][D] inputs): instruction q reads
+    // the byte offsets dma_blocks would use.
     auto plan_of = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo, int key) {
       DmaPlan<PW> pl;
       pl.lds = __builtin_amdgcn_readfirstlane(
           (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
       pl.r = r;
-      if constexpr (SLAB_IN) {
-        if (key >= p.S) {
 #pragma unroll
-          for (int q = 0; q < PW; ++q) pl.addr[q] = in_bytes + lo[q];
-        } else {
-          const uint32_t ps = (__umulhi((uint32_t)key, p.sp_magic) + key) >> p.sp_shift;
-          const uint32_t base = ((ps * p.B + b) * p.Sp + (key - ps * p.Sp)) * rowstride + head_col;
-          const int left = (int)((ps + 1) * p.Sp) - key;
-          const uint32_t delta = (uint32_t)(p.B - 1) * p.Sp * rowstride;
-#pragma unroll
-          for (int q = 0; q < PW; ++q)
-            pl.addr[q] = base + lo[q] + (row0 + q * (64 / Tile<D>::CH) >= left ? delta : 0u);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < PW; ++q) pl.addr[q] = (uint32_t)key * (D * 2) + lo[q];
-      }
+      for (int q = 0; q < PW; ++q) pl.addr[q] = (uint32_t)key * (D * 2) + lo[q];
       return pl;
     };
     // Masked units: this group's stream of kept stages, and the first keys of
@@ -695,21 +680,29 @@ void fa_fwd_pp_kernel(FwdParams p) {
       }
     };
     // The DMA issued in region S(n) (SLOT = n % NBUF), after the barrier
-    // that ends every wave's reads of the slots it refills: whole units at
-    // the region's start, split units at four points of its softmax.
+    // that ends every wave's reads of the slots it refills: at the region's
+    // start, except that split units with [B][H][S][D] inputs spread theirs
+    // over four points of the softmax (split_plans; measured faster there,
+    // slower for whole units and for slab inputs, whose per-lane slab
+    // addresses would then stay live through the softmax).
     // Whole units: K stage n + 3 (group 0) or V stage n + 3 (group 1) into
     // the slot that stage n - 1 freed.  Split units, each group on its own
     // stream: K stage n + 2 into the slot of K stage n (read in M(n - 1)) and
     // V stage n + 1 into the slot of V stage n - 1 (read in M(n - 1)).
     auto stage_dma = [&](auto SLOT, int n) {
       constexpr int slot = decltype(SLOT)::value;
-      if (grp == 0) {
+      if (SPLIT) {
+        dma_k(slot, MASKED ? key_n[2] : key_of(n + 2));
+        dma_v((slot + 1) % NBUF, MASKED ? key_n[1] : key_of(n + 1));
+      } else if (grp == 0) {
+
         dma_k((slot + 3) % NBUF, key_of(n + 3));
       } else {
         dma_v((slot + 3) % NBUF, key_of(n + 3));
       }
     };
-    // Split units: the same stages as DmaPlans, issued during the softmax.
+    // Split units, [B][H][S][D] inputs: the same stages as DmaPlans, issued
+    // during the softmax.
     struct SplitPlans { DmaPlan<PW> k, v; };
     auto split_plans = [&](auto SLOT, int n) {
       constexpr int slot = decltype(SLOT)::value;
@@ -765,7 +758,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
     // units: S(n - 1)) before the barrier that precedes its first readers.
     auto region_s = [&](auto SLOT, int n, StageProbs<NEG>& sm) {
       const int key0 = MASKED ? key_n[0] : (own * nsh + n) * BN;
-      if constexpr (SPLIT) {
+      if constexpr (SPLIT && !SLAB_IN) {
         const SplitPlans pl = split_plans(SLOT, n);
         mask_tail(s, key0, p.S, g, fill);
         sm.template compute<true>(s, c, m_run, l_run, [&](int j) {
