@@ -776,8 +776,8 @@ void fa_fwd_pp_kernel(FwdParams p) {
       wait_vm<NDMA>();
     };
     // Region M(n): the scores of stage n + 1 (K stage n + 1) and PV of stage
-    // n (V stage n), interleaved: QK^T MFMA i after PV MFMA i.  After the last
-    // stage the QK^T MFMAs read a buffer of zeros and their result is unused.
+    // n (V stage n).  After the last stage the QK^T MFMAs read a buffer of
+    // zeros and their result is unused.
     auto region_m = [&](auto SLOT, const StageProbs<NEG>& sm) {
       constexpr int slot = decltype(SLOT)::value;
       // Raised wave priority while this wave issues MFMAs: when both waves
@@ -796,23 +796,50 @@ void fa_fwd_pp_kernel(FwdParams p) {
       constexpr int LEAD = FA_MLEAD;
       auto ka_read = [&](int i) { return k_operand<D>(kn, i & 1, i >> 1, l32, g); };
       auto va_read = [&](int j) { return v_operand<D>(vt, j / NDB, j % NDB, lane); };
-      bf16x8 ka[NA], va[NB];
-#pragma unroll
-      for (int i = 0; i < LEAD; ++i) {
-        va[i] = va_read(i);
-        ka[i] = ka_read(i);
-      }
-#pragma unroll
-      for (int i = 0; i < NA; ++i) {
-        if (i + LEAD < NA) {
-          va[i + LEAD] = va_read(i + LEAD);
-          ka[i + LEAD] = ka_read(i + LEAD);
-        }
-        acc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], sm.p_operand(i / NDB),
-                                                               acc[i % NDB], 0, 0, 0);
-        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i >> 1],
+      // Whole units interleave the two products, QK^T MFMA i before PV MFMA
+      // i; split units issue all of QK^T first, then PV.  Each accumulator
+      // sees the same operands in the same order either way (the results
+      // are bit-identical); these orders measured fastest for each form.
+      auto qk = [&](int i, const bf16x8& a) {
+        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i >> 1],
                                                            i < 2 ? f32x16{} : s[i & 1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto pv = [&](int j, const bf16x8& a) {
+        acc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sm.p_operand(j / NDB),
+                                                               acc[j % NDB], 0, 0, 0);
+      };
+      if constexpr (!SPLIT) {
+        bf16x8 ka[NA], va[NB];
+#pragma unroll
+        for (int i = 0; i < LEAD; ++i) {
+          va[i] = va_read(i);
+          ka[i] = ka_read(i);
+        }
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+          if (i + LEAD < NA) {
+            va[i + LEAD] = va_read(i + LEAD);
+            ka[i + LEAD] = ka_read(i + LEAD);
+          }
+          qk(i, ka[i]);
+          pv(i, va[i]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        // Operand t: QK^T MFMA t (t < NA) or PV MFMA t - NA, read 2 LEAD ahead.
+        bf16x8 op[NA + NB];
+        auto rd = [&](int t) { op[t] = t < NA ? ka_read(t) : va_read(t - NA); };
+#pragma unroll
+        for (int t = 0; t < 2 * LEAD; ++t) rd(t);
+#pragma unroll
+        for (int t = 0; t < NA + NB; ++t) {
+          if (t + 2 * LEAD < NA + NB) rd(t + 2 * LEAD);
+          if (t < NA)
+            qk(t, op[t]);
+          else
+            pv(t - NA, op[t]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       __builtin_amdgcn_s_setprio(0);
     };
