@@ -246,8 +246,12 @@ __device__ __forceinline__ int xcd_slot(int block, int G) {
 // the row's 2K stages, stream 1 the second.  next() gives the first key of
 // the stream's next stage, or S once the stream's K stages are used up.  Bits
 // for tiles past the row's end are ignored.  All state is wave-uniform.
+// The mask words are read through the constant address space, which makes
+// them scalar loads: their wait (lgkmcnt) leaves the stream's K/V DMA in
+// flight, where a vector load's vmcnt(0) would wait for all of it.
+typedef const __attribute__((address_space(4))) uint64_t* mask_row_t;
 struct KeptStages {
-  const uint64_t* row;
+  mask_row_t row;
   int mw, w, half, left, S;
   uint64_t bits, last_mask;
 
@@ -255,7 +259,7 @@ struct KeptStages {
 
   // Positions the stream; returns K, the number of kept tiles in the row.
   __device__ int init(const uint64_t* r, int nmt, int words, int seq, int stream) {
-    row = r;
+    row = (mask_row_t)r;
     mw = words;
     S = seq;
     last_mask = (nmt & 63) ? (1ull << (nmt & 63)) - 1 : ~0ull;
