@@ -324,26 +324,30 @@ def test_deterministic_and_stream():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("case", ["video share", "image share", "whole tiles + half-tiles"])
+@pytest.mark.parametrize("case", ["video share", "image share", "whole tiles + half-tiles",
+                                  "block-sparse video share", "block mask, head dim 64"])
 def test_repeated_calls_bit_identical(case):
     """Repeated calls on the same inputs return the same bits.  Waves that
     race on an LDS buffer (a refill landing while another wave still reads
     the stage) show up as run-to-run differences, so this covers the whole-
-    and split-tile launches over many calls."""
+    and split-tile launches and the masked units over many calls."""
     import flashattention_output_re_amd as fa
-    shapes = {"video share": (1, 5, 32760, 128, 8), "image share": (1, 3, 4096, 128, 8),
-              "whole tiles + half-tiles": (1, _cus() + 5, 300, 128, 3)}
-    B, H, S, D, P = shapes[case]
-    say(f"[repeat] {case}: B={B} H={H} S={S} D={D} P={P}")
+    shapes = {"video share": (1, 5, 32760, 128, 8, None), "image share": (1, 3, 4096, 128, 8, None),
+              "whole tiles + half-tiles": (1, _cus() + 5, 300, 128, 3, None),
+              "block-sparse video share": (1, 5, 32760, 128, 8, 0.3),
+              "block mask, head dim 64": (2, 3, 9000, 64, 4, 0.5)}
+    B, H, S, D, P, keep = shapes[case]
+    say(f"[repeat] {case}: B={B} H={H} S={S} D={D} P={P} keep={keep}")
     q, k, v = (to_dev(t) for t in wl.random_qkv(B, H, S, D, seed=S + H))
+    mask = None if keep is None else mask_to_dev(wl.pack_mask(wl.tile_mask_bool(H, S, keep, seed=S + H)))
     scale = 1.0 / math.sqrt(D)
     first = torch.empty((P, B, S // P, H, D), dtype=torch.bfloat16, device=q.device)
-    fa.attn_fwd_relayout_async(q, k, v, first, B, H, S, D, P, scale, None)
+    fa.attn_fwd_relayout_async(q, k, v, first, B, H, S, D, P, scale, mask)
     out = torch.empty_like(first)
     calls = 10 if S > 10000 else 30
     for i in range(calls):
         out.fill_(0)
-        fa.attn_fwd_relayout_async(q, k, v, out, B, H, S, D, P, scale, None)
+        fa.attn_fwd_relayout_async(q, k, v, out, B, H, S, D, P, scale, mask)
         assert torch.equal(out.view(torch.int16), first.view(torch.int16)), f"{case}: call {i + 1} differs"
     torch.cuda.synchronize()
 
