@@ -34,8 +34,11 @@
 //   chunks (conflict-free operand reads).
 //
 // Softmax runs in the log2 domain (c = scale * log2 e, p = exp2(s c - m)).
-// The running max is only raised when some row of the wave exceeds it by more
-// than kTau (2^8 headroom for p); the final division by the row sum makes the
+// The probabilities are first taken against the running max as it stands; it
+// is only raised, and the stage recomputed, when some lane's sum over the
+// stage passes kRaise = 2^8.  So no probability exceeds 2^8, and a key that
+// comes to dominate its row is re-centred to weigh exactly 1 (its bf16
+// rounding is then exact).  The final division by the row sum makes the
 // result independent of which max was used.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,7 +55,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128;          // rows of a mask tile (queries and keys); masked unit size
 constexpr int BN = 64;           // keys per LDS stage
-constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
+constexpr float kRaise = 256.0f;   // a lane's stage sum that raises the running max
+
 // Tuning knob, overridable at build time (-D): operand reads issued ahead of
 // their MFMA in the MFMA region.
 #ifndef FA_MLEAD
@@ -341,11 +345,13 @@ __device__ __forceinline__ void qk_mfma(f32x16 (&s)[2], const uint16_t* ks,
 
 // Online softmax of one K/V stage as one block of VALU work, run in a region
 // of its own beside another wave's MFMAs.  This lane holds 32 scores of its
-// query (two 32-key blocks x 16).  The row extreme (max for c > 0, min for
-// c < 0) over four partial chains, the running max raised only when some row
-// of the wave exceeds it by more than kTau, all 32 probabilities
-// exp2(s c - m) as bf16 pairs (the B operand of the PV MFMAs), and their sum
-// over four partial sums folded into the running row sum.
+// query (two 32-key blocks x 16).  All 32 probabilities exp2(s c - m) as
+// bf16 pairs (the B operand of the PV MFMAs) and their sum over four partial
+// chains, against the running max m as it stands: no row extreme stands
+// between the scores and the exponentials.  Only when some lane's sum passes
+// kRaise (or is infinite, as at the first stage) does the wave take the
+// row extreme (max for c > 0, min for c < 0), raise m to it and recompute
+// the stage from the scores, which stay in sc.
 template <bool NEG>
 struct StageProbs {
   float alpha = 1.0f;
@@ -367,39 +373,52 @@ struct StageProbs {
       }
     };
     point(0);
-    float e[4];
+    // The probabilities of the stage against a max m, as bf16 pairs in pk,
+    // and their sum over four partial chains.
+    auto probs = [&](float m, bool points) {
+      const float neg_m = -m;
+      float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int mb = k >> 1, r0 = 8 * (k & 1);
-      float x = sc[mb][r0];
+      for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int r = 1; r < 8; ++r) x = NEG ? fminf(x, sc[mb][r0 + r]) : fmaxf(x, sc[mb][r0 + r]);
-      e[k] = x;
+        for (int pi = 0; pi < 8; ++pi) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][2 * pi], c, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][2 * pi + 1], c, neg_m));
+          ls[(2 * pi) & 3] += p0;
+          ls[(2 * pi + 1) & 3] += p1;
+          pk[8 * mb + pi] = pack_bf16(p0, p1);
+          if (points && mb == 0 && pi == 3) point(1);
+        }
+        if (points) point(2 + mb);
+      }
+      return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    // First against the running max as it stands; only when some lane's sum
+    // passes kRaise (or overflows) is the max raised to the row's extreme and
+    // the stage recomputed (the scores are still in sc).
+    float l_stage = probs(m_run, true);
+    rescale = __builtin_amdgcn_ballot_w64(l_stage > kRaise) != 0;
+    if (rescale) {
+      float e[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int mb = k >> 1, r0 = 8 * (k & 1);
+        float x = sc[mb][r0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) x = NEG ? fminf(x, sc[mb][r0 + r]) : fmaxf(x, sc[mb][r0 + r]);
+        e[k] = x;
+      }
+      float ex = NEG ? fminf(fminf(e[0], e[1]), fminf(e[2], e[3]))
+                     : fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3]));
+      ex = NEG ? halves_min(ex) : halves_max(ex);
+      const float m_new = fmaxf(m_run, ex * c);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_stage = probs(m_new, false);
+      l_run = l_run * alpha + l_stage;
+    } else {
+      l_run += l_stage;
     }
-    float ex = NEG ? fminf(fminf(e[0], e[1]), fminf(e[2], e[3]))
-                   : fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3]));
-    ex = NEG ? halves_min(ex) : halves_max(ex);
-    const float m_cand = fmaxf(m_run, ex * c);
-    rescale = __builtin_amdgcn_ballot_w64(m_cand > m_run + kTau) != 0;
-    const float m_use = rescale ? m_cand : m_run;
-    alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_use;
-    const float neg_m = -m_use;
-    point(1);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[mb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][r], c, neg_m));
-      point(2 + mb);
-    }
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ls[r & 3] += sc[mb][r];
-#pragma unroll
-    for (int pi = 0; pi < 16; ++pi) pk[pi] = pack_bf16(sc[pi >> 3][2 * (pi & 7)], sc[pi >> 3][2 * (pi & 7) + 1]);
-    l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
     // Keep all of it in the softmax region: without these uses the compiler
     // sinks the exponentials past the barrier into the MFMA region.
 #pragma unroll
@@ -728,11 +747,13 @@ void fa_fwd_pp_kernel(FwdParams p) {
     f32x16 acc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-    // A masked stream may meet a stage with no key at all (the second half of
-    // a kept last tile shorter than 64 keys) before any other: a finite
-    // starting max keeps its weights exp2(-inf) = 0 rather than NaN, and is
-    // replaced by the first real maximum (the rescale factor is then 0).
-    float m_run = MASKED ? -3.0e38f : -__builtin_inff();
+    // A finite starting max: the first stage's probabilities overflow against
+    // it and raise it to the row's extreme (the rescale factor is then 0),
+    // while keys past the end (fill, -inf after scaling) and a masked stream's
+    // stage with no key at all (the second half of a kept last tile shorter
+    // than 64 keys) weigh exp2(-inf) = 0 rather than NaN.
+    float m_run = -3.0e38f;
+
     float l_run = 0.0f;
 
     // Prologue: K stages 0 and 1 and V stage 0 (SPLIT: each group, its own
