@@ -874,13 +874,18 @@ void fa_fwd_pp_kernel(FwdParams p) {
       region_s(SLOT, n, sm);
       barrier_keep_dma();
       region_m(SLOT, sm);
-      barrier_keep_dma();
+      // Masked units advance their stream's stage keys here, at the end of
+      // the MFMA region, rather than at the start of the next softmax region:
+      // the scalar mask walk then costs the MFMA wave (whose operand reads
+      // are all consumed by now) instead of the softmax wave.
       if (MASKED) {
         key_n[0] = key_n[1];
         key_n[1] = key_n[2];
         key_n[2] = kept.next();
       }
+      barrier_keep_dma();
     };
+
 
     for (int n = 0; n < nloop; n += NBUF) {
       stage(std::integral_constant<int, 0>{}, n);
