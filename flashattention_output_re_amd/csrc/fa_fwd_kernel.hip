@@ -718,7 +718,6 @@ void fa_fwd_pp_kernel(FwdParams p) {
         dma_k(slot, MASKED ? key_n[2] : key_of(n + 2));
         dma_v((slot + 1) % NBUF, MASKED ? key_n[1] : key_of(n + 1));
       } else if (grp == 0) {
-
         dma_k((slot + 3) % NBUF, key_of(n + 3));
       } else {
         dma_v((slot + 3) % NBUF, key_of(n + 3));
