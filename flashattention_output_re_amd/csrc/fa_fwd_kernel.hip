@@ -717,11 +717,18 @@ void fa_fwd_pp_kernel(FwdParams p) {
       if (SPLIT) {
         dma_k(slot, MASKED ? key_n[2] : key_of(n + 2));
         dma_v((slot + 1) % NBUF, MASKED ? key_n[1] : key_of(n + 1));
+      } else if constexpr (!SLAB_IN) {
+        // One code path for both groups (the tensor and slot selected, not
+        // branched on): the softmax wave takes no branch to issue its DMA.
+        constexpr int sl = (slot + 3) % NBUF;
+        uint16_t* const dst = (grp == 0 ? kbuf(sl) : vbuf(sl)) + 64 * 8 * PW * wq;
+        dma_blocks<PW>(dst, grp == 0 ? rk : rv, (uint32_t)key_of(n + 3) * (D * 2), koff);
       } else if (grp == 0) {
         dma_k((slot + 3) % NBUF, key_of(n + 3));
       } else {
         dma_v((slot + 3) % NBUF, key_of(n + 3));
       }
+
     };
     // Split units, [B][H][S][D] inputs: the same stages as DmaPlans, issued
     // during the softmax.
