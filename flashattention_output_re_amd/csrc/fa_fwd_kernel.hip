@@ -398,7 +398,8 @@ struct StageProbs {
     // the stage recomputed (the scores are still in sc).
     float l_stage = probs(m_run, true);
     rescale = __builtin_amdgcn_ballot_w64(l_stage > kRaise) != 0;
-    if (rescale) {
+    // Rare: laid out of line, so the common path takes no branch.
+    if (__builtin_expect(rescale, 0)) {
       float e[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -435,7 +436,9 @@ struct StageProbs {
 // Keys >= S of a ragged last stage do not exist: their scores become fill
 // (fill * c = -inf).  Lane (l32, g) holds keys 32 mb + 8 (r / 4) + 4 g + r % 4.
 __device__ __forceinline__ void mask_tail(f32x16 (&sc)[2], int stage_key0, int S, int g, float fill) {
-  if (stage_key0 + BN <= S) return;
+  // The common case first: the tail code is laid out of line, so a full
+  // stage takes no branch here.
+  if (__builtin_expect(stage_key0 + BN <= S, 1)) return;
   const int key0 = stage_key0 + 4 * g;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -817,7 +820,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
       __builtin_amdgcn_s_setprio(2);
       const uint16_t* const kn = kbuf((slot + 1) % NBUF);
       const uint16_t* const vt = vbuf(slot);
-      if (sm.rescale) {
+      if (__builtin_expect(sm.rescale, 0)) {   // rare: out of line
 #pragma unroll
         for (int i = 0; i < NDB; ++i)
 #pragma unroll
