@@ -39,10 +39,17 @@ SIGNATURES = {
     "attn_fwd_plain": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P],
     "relayout_to_slabs_async": [_P, _P, _I, _I, _I, _I, _I, _P],
     "relayout_to_slabs": [_P, _P, _I, _I, _I, _I, _I],
-    "burst_gap_run_async": [_P, _P, _I, _I, _I, _I, _I, _P],
+    "burst_gap_run_async": [_P, _P, _I, _I, _I, _I, _I, _I, _P],
+    "attn_fwd_relayout_instrumented_async": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _P,
+                                             ctypes.c_int64, _P, _P],
+    "attn_instrumented_stamp_words": [_I, _I, _I],
     "attn_status_string": [_I],
     "attn_abi_version": [],
 }
+
+
+RESTYPES = {"attn_status_string": ctypes.c_char_p,
+            "attn_instrumented_stamp_words": ctypes.c_int64}
 
 
 class FaError(RuntimeError):
@@ -65,7 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             for name, args in SIGNATURES.items():
                 fn = getattr(lib, name)
                 fn.argtypes = args
-                fn.restype = ctypes.c_char_p if name == "attn_status_string" else ctypes.c_int
+                fn.restype = RESTYPES.get(name, ctypes.c_int)
             _lib = lib
         return _lib
 
@@ -210,6 +217,36 @@ def relayout_to_slabs(plain, out_slabs, B, H, S, D, P):
     _check_relayout(plain, out_slabs, B, H, S, D, P)
     st = load_library().relayout_to_slabs(_ptr(plain), _ptr(out_slabs), B, H, S, D, P)
     _raise(st, "relayout_to_slabs")
+
+
+def attn_instrumented_stamp_words(B: int, H: int, S: int) -> int:
+    return int(load_library().attn_instrumented_stamp_words(B, H, S))
+
+
+BOUNDARY_PIGGYBACK, BOUNDARY_COUPLED, BOUNDARY_ORDERED = 0, 1, 2
+
+
+def attn_fwd_relayout_instrumented_async(q, k, v, out_slabs, B, H, S, D, P, scale, mask=None,
+                                         boundary=BOUNDARY_PIGGYBACK, stamps=None, stream=None):
+    """The fused call with per-tile timestamps (include/fa_instrument.h).
+    boundary: 0 piggybacked (the product kernel's), 1 completion-coupled,
+    2 stores then the next prologue with one wait.  stamps: int32 device
+    tensor of at least attn_instrumented_stamp_words(B, H, S) elements.
+    Returns the unit counts of the call's two launches."""
+    if P > 0 and S % P == 0:
+        for n, t in (("q", q), ("k", k), ("v", v)):
+            _check_tensor(n, t, (B, H, S, D))
+        _check_tensor("out_slabs", out_slabs, (P, B, S // P, H, D))
+        _check_mask(mask, H, S)
+    if stamps is None or stamps.dtype not in (torch.int32, torch.uint32) or not stamps.is_cuda \
+            or not stamps.is_contiguous():
+        raise ValueError("stamps must be a contiguous 32-bit device tensor")
+    units = (ctypes.c_int * 2)()
+    st = load_library().attn_fwd_relayout_instrumented_async(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out_slabs), B, H, S, D, P, float(scale), _ptr(mask),
+        int(boundary), _ptr(stamps), stamps.numel(), units, _stream(stream))
+    _raise(st, "attn_fwd_relayout_instrumented_async")
+    return int(units[0]), int(units[1])
 
 
 def attention_relayout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: int,

@@ -33,9 +33,10 @@ WARMUP_BURSTS = 4          # bursts ignored when taking steady-state medians
 
 
 def run(dst: torch.Tensor, producers: int, bytes_per_producer: int, bursts: int,
-        gap_iters: int, nontemporal: bool = False):
+        gap_iters: int, nontemporal: bool = False, coupled: bool = False):
     """One launch; returns (issue_s, gap_s, clock_hz, complete_s), the first two
-    [producers][bursts] arrays in seconds."""
+    [producers][bursts] arrays in seconds.  coupled: each burst waits for its
+    stores to complete before its issue time is taken."""
     need = bursts * producers * bytes_per_producer
     if dst.numel() * dst.element_size() < need:
         raise ValueError("dst too small")
@@ -43,7 +44,7 @@ def run(dst: torch.Tensor, producers: int, bytes_per_producer: int, bursts: int,
                         device=dst.device)
     st = binding.load_library().burst_gap_run_async(
         binding._ptr(dst), binding._ptr(times), producers, bytes_per_producer, bursts, gap_iters,
-        int(bool(nontemporal)), binding._stream(None))
+        int(bool(nontemporal)), int(bool(coupled)), binding._stream(None))
     binding._raise(st, "burst_gap_run_async")
     torch.cuda.synchronize()
     t = times.cpu().numpy().astype(np.int64)

@@ -6,7 +6,10 @@
 // does not wait for the stores to complete (no release fence), so it is the
 // sender-visible time the pages model: stores are accepted and drain while
 // the producer moves on.  The gap is a dependent FMA chain whose length the
-// caller sets.  Stores complete (vmcnt) only at the very end.
+// caller sets.  Stores complete (vmcnt) only at the very end -- unless the
+// caller asks for the completion-coupled form, where every wave waits for
+// its burst's stores to complete (vmcnt(0)) before the barrier that takes the
+// issue time, so a burst is only over once it has drained.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -21,7 +24,7 @@ constexpr int kLdsBytes = 96 * 1024;   // one producer per CU
 constexpr uint32_t kMagic = 0x9E3779B9u;
 
 struct BurstGapParams {
-  int producers, chunks, bursts, gap_iters, nontemporal;
+  int producers, chunks, bursts, gap_iters, nontemporal, coupled;
 };
 
 __device__ __forceinline__ void barrier_no_fence() {
@@ -53,7 +56,8 @@ __global__ __launch_bounds__(kThreads) void burst_gap_kernel(u32x4* dst, uint64_
       for (int c = tid; c < p.chunks; c += kThreads)
         base[c] = u32x4{(uint32_t)i, (uint32_t)k, (uint32_t)c, kMagic};
     }
-    barrier_no_fence();   // every wave has issued its stores
+    if (p.coupled) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores completed
+    barrier_no_fence();   // every wave has issued (coupled: completed) its stores
     const uint64_t t1 = __builtin_amdgcn_s_memtime();
     for (int g = 0; g < p.gap_iters; ++g) {
       acc = __builtin_fmaf(acc, 0.999999f, 1e-6f);
@@ -80,18 +84,18 @@ __global__ __launch_bounds__(kThreads) void burst_gap_kernel(u32x4* dst, uint64_
 
 extern "C" int burst_gap_run_async(void* dst, uint64_t* times, int producers,
                                    int bytes_per_producer, int bursts, int gap_iters,
-                                   int nontemporal, void* stream) {
+                                   int nontemporal, int coupled, void* stream) {
   if (!dst || !times) return FA_EINVAL;
   if (producers < 1 || producers > 4096 || bursts < 1 || bursts > 4096 || gap_iters < 0 ||
       bytes_per_producer <= 0 || bytes_per_producer % 4096 != 0 ||
-      (nontemporal != 0 && nontemporal != 1))
+      (nontemporal != 0 && nontemporal != 1) || (coupled != 0 && coupled != 1))
     return FA_EINVAL;
   if ((reinterpret_cast<uintptr_t>(dst) & 15) || (reinterpret_cast<uintptr_t>(times) & 7))
     return FA_EALIGN;
   if ((uint64_t)bursts * producers * bytes_per_producer > (1ull << 40)) return FA_ERANGE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FA_EDEVICE;
-  BurstGapParams p{producers, bytes_per_producer / 16, bursts, gap_iters, nontemporal};
+  BurstGapParams p{producers, bytes_per_producer / 16, bursts, gap_iters, nontemporal, coupled};
   hipLaunchKernelGGL(burst_gap_kernel, dim3(producers), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<u32x4*>(dst), times, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ELAUNCH;

@@ -8,6 +8,7 @@
 #include <mutex>
 
 #include "../../include/fa_relayout.h"
+#include "../../include/fa_instrument.h"
 #include "fa_fwd_kernel.h"
 #include "fa_relayout_kernel.h"
 
@@ -15,6 +16,10 @@ namespace {
 
 constexpr int kQTile = 128;
 constexpr int kMaxDevices = 64;
+// uint32 words of timestamps per unit of an instrumented launch: one record
+// of 8 words for each of the 8 waves.
+constexpr int kStampWordsPerUnit = 64;
+constexpr float kMaxScale = 18446744073709551616.0f;   // 2^64
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -23,7 +28,9 @@ int validate(const void* q, const void* k, const void* v, const void* out, int B
              int D, int P, float scale, const uint64_t* mask) {
   if (!q || !k || !v || !out) return FA_EINVAL;
   if (B <= 0 || H <= 0 || S <= 0 || P <= 0) return FA_EINVAL;
-  if (!std::isfinite(scale)) return FA_EINVAL;
+  // |scale| <= 2^64 keeps scale * log2(e) * score inside fp32 for every
+  // score below 2^62 in magnitude; larger scales are rejected.
+  if (!std::isfinite(scale) || std::fabs(scale) > kMaxScale) return FA_EINVAL;
   if (D != 64 && D != 128) return FA_EUNSUPPORTED;
   if (S % P != 0) return FA_EDIV;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
@@ -89,19 +96,47 @@ void div_magic(uint32_t d, uint32_t* magic, int* shift) {
   *magic = (uint32_t)((((uint64_t)1 << 32) * ((1ull << l) - d)) / d + 1);
 }
 
-int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* out, int B, int H,
-        int S, int D, int P, float scale, const uint64_t* mask, hipStream_t stream,
-        bool slab_in = false) {
+// How one dense call splits into launches: `whole` units of whole 256-query
+// tiles on up to `cap` workgroups, then (split_units > 0) the last round's
+// tiles as 2 x tail half tiles in a second launch on up to `split_cap`.
+struct DensePlan {
+  int whole_units = 0, split_units = 0, cap = 0, split_cap = 0;
+};
+
+// Launch geometry of a call with params p (units = every tile): the number
+// of units per launch and the persistent grid caps, or FA_EDEVICE.
+int plan_call(int D, fa::StoreMode mode, bool masked, const fa::FwdParams& p, DensePlan* plan) {
+  const fa::Variant var = masked ? fa::Variant::Masked : fa::Variant::Whole;
+  const int cap = grid_cap_for(D, mode, var);
+  if (cap <= 0) return FA_EDEVICE;
+  *plan = DensePlan{};
+  plan->cap = cap;
+  plan->whole_units = p.units;
+  if (masked) return FA_OK;
+  // Dense: whole 256-query tiles fill `cap` CUs per round.  When the last
+  // round would keep at most half of the CUs busy, its R tiles run instead as
+  // 2R half-tiles with the keys split inside each workgroup (about half the
+  // time of a whole tile), in a second launch on the same stream.
+  const int tail = p.units % cap;
+  const int stages = (p.S + 63) / 64;
+  if (tail == 0 || 2 * tail > cap || stages < 2) return FA_OK;
+  const int split_cap = grid_cap_for(D, mode, fa::Variant::Split);
+  if (split_cap <= 0) return FA_EDEVICE;
+  plan->whole_units = p.units - tail;
+  plan->split_units = 2 * tail;
+  plan->split_cap = split_cap;
+  return FA_OK;
+}
+
+// Validated call -> kernel parameters (every tile as one launch's units).
+int make_params(fa::StoreMode mode, const void* q, const void* k, const void* v, void* out,
+                int B, int H, int S, int D, int P, float scale, const uint64_t* mask, bool slab_in,
+                fa::FwdParams* pp) {
   int st = validate(q, k, v, out, B, H, S, D, P, scale, mask);
   if (st == FA_OK && slab_in) st = validate_slab_in(B, H, S, D, P);
   if (st != FA_OK) return st;
-  // Dense attention runs on 256-query tiles; a block mask gives each
-  // 128-query tile its own key set, so masked calls run on 128-query tiles
-  // with the keys split between the two wave groups.
-  const fa::Variant var = mask ? fa::Variant::Masked : fa::Variant::Whole;
-  const int cap = grid_cap_for(D, mode, var);
-  if (cap <= 0) return FA_EDEVICE;
-  fa::FwdParams p;
+  fa::FwdParams& p = *pp;
+  p = fa::FwdParams{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -113,7 +148,10 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   p.P = P;
   p.Sp = S / P;
   div_magic((uint32_t)p.Sp, &p.sp_magic, &p.sp_shift);
-  const int rows = fa::tile_rows(var);
+  // Dense attention runs on 256-query tiles; a block mask gives each
+  // 128-query tile its own key set, so masked calls run on 128-query tiles
+  // with the keys split between the two wave groups.
+  const int rows = fa::tile_rows(mask ? fa::Variant::Masked : fa::Variant::Whole);
   p.nqt = (S + rows - 1) / rows;
   p.units = B * H * p.nqt;
   p.unit_base = 0;
@@ -124,28 +162,44 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   // that |s| * c rounds away against 1 gives the same weights bit for bit,
   // and keeps (-inf) * c = -inf for the keys past S.
   if (p.c == 0.0f) p.c = 1e-30f;
-  if (mask)
-    return fa::launch_fwd(D, mode, var, p, cap, stream, slab_in) == 0 ? FA_OK : FA_ELAUNCH;
+  p.stamps = nullptr;
+  return FA_OK;
+}
 
-  // Dense: whole 256-query tiles fill `cap` CUs per round.  When the last
-  // round would keep at most half of the CUs busy, its R tiles run instead as
-  // 2R half-tiles with the keys split inside each workgroup (about half the
-  // time of a whole tile), in a second launch on the same stream.
-  const int tail = p.units % cap;
-  const int stages = (S + 63) / 64;
-  if (tail == 0 || 2 * tail > cap || stages < 2)
-    return fa::launch_fwd(D, mode, var, p, cap, stream, slab_in) == 0 ? FA_OK : FA_ELAUNCH;
-  const int split_cap = grid_cap_for(D, mode, fa::Variant::Split);
-  if (split_cap <= 0) return FA_EDEVICE;
-  fa::FwdParams whole = p;
-  whole.units = p.units - tail;
-  if (whole.units > 0 && fa::launch_fwd(D, mode, var, whole, cap, stream, slab_in) != 0)
-    return FA_ELAUNCH;
-  fa::FwdParams half = p;
-  half.units = 2 * tail;
-  half.unit_base = p.units - tail;
-  return fa::launch_fwd(D, mode, fa::Variant::Split, half, split_cap, stream, slab_in) == 0
-             ? FA_OK : FA_ELAUNCH;
+// Enqueue the launches of a call.  instr != 0: timestamped instances, the
+// records of the split launch following those of the whole-tile launch.
+int launch_call(int D, fa::StoreMode mode, const fa::FwdParams& p, const DensePlan& plan,
+                hipStream_t stream, bool slab_in, int instr) {
+  const bool masked = p.mask != nullptr;
+  const fa::Variant var = masked ? fa::Variant::Masked : fa::Variant::Whole;
+  if (plan.whole_units > 0) {
+    fa::FwdParams whole = p;
+    whole.units = plan.whole_units;
+    if (fa::launch_fwd(D, mode, var, whole, plan.cap, stream, slab_in, instr) != 0)
+      return FA_ELAUNCH;
+  }
+  if (plan.split_units > 0) {
+    fa::FwdParams half = p;
+    half.units = plan.split_units;
+    half.unit_base = p.units - plan.split_units / 2;
+    if (instr) half.stamps = p.stamps + (size_t)plan.whole_units * kStampWordsPerUnit;
+    if (fa::launch_fwd(D, mode, fa::Variant::Split, half, plan.split_cap, stream, slab_in,
+                       instr) != 0)
+      return FA_ELAUNCH;
+  }
+  return FA_OK;
+}
+
+int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* out, int B, int H,
+        int S, int D, int P, float scale, const uint64_t* mask, hipStream_t stream,
+        bool slab_in = false) {
+  fa::FwdParams p;
+  int st = make_params(mode, q, k, v, out, B, H, S, D, P, scale, mask, slab_in, &p);
+  if (st != FA_OK) return st;
+  DensePlan plan;
+  st = plan_call(D, mode, mask != nullptr, p, &plan);
+  if (st != FA_OK) return st;
+  return launch_call(D, mode, p, plan, stream, slab_in, 0);
 }
 
 int validate_relayout(const void* plain, const void* out, int B, int H, int S, int D, int P) {
@@ -239,10 +293,42 @@ int relayout_to_slabs(const void* plain, void* out_slabs, int B, int H, int S, i
   return finish_blocking(run_relayout(plain, out_slabs, B, H, S, D, P, nullptr));
 }
 
+int attn_fwd_relayout_instrumented_async(const void* q, const void* k, const void* v,
+                                         void* out_slabs, int B, int H, int S, int D, int P,
+                                         float scale, const uint64_t* mask, int boundary,
+                                         uint32_t* stamps, int64_t stamp_words,
+                                         int* launch_units, void* stream) {
+  fa::FwdParams p;
+  int st = make_params(fa::StoreMode::Slab, q, k, v, out_slabs, B, H, S, D, P, scale, mask, false,
+                       &p);
+  if (st != FA_OK) return st;
+  if (boundary < 0 || boundary > 2) return FA_EINVAL;
+  if (!stamps) return FA_EINVAL;
+  if (D != 128 || !(scale > 0.0f)) return FA_EUNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(stamps) & 15) return FA_EALIGN;
+  if (stamp_words < attn_instrumented_stamp_words(B, H, S)) return FA_ERANGE;
+  DensePlan plan;
+  st = plan_call(D, fa::StoreMode::Slab, mask != nullptr, p, &plan);
+  if (st != FA_OK) return st;
+  p.stamps = stamps;
+  if (launch_units) {
+    launch_units[0] = plan.whole_units;
+    launch_units[1] = plan.split_units;
+  }
+  return launch_call(D, fa::StoreMode::Slab, p, plan, static_cast<hipStream_t>(stream), false,
+                     boundary + 1);
+}
+
+int64_t attn_instrumented_stamp_words(int B, int H, int S) {
+  if (B <= 0 || H <= 0 || S <= 0) return 0;
+  return (int64_t)kStampWordsPerUnit * B * H * ((S + kQTile - 1) / kQTile + 1);
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
-    case FA_EINVAL: return "invalid argument (null tensor, non-positive size or non-finite scale)";
+    case FA_EINVAL:
+      return "invalid argument (null tensor, non-positive size, or scale not finite or beyond 2^64)";
     case FA_EDIV: return "S is not a multiple of the slab count P";
     case FA_EUNSUPPORTED:
       return "unsupported shape (D must be 64 or 128; slab inputs need S/P >= 64)";

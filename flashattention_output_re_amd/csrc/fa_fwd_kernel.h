@@ -35,13 +35,20 @@ struct FwdParams {
   // for n < 2^31.
   uint32_t sp_magic;
   int sp_shift;
+  // Instrumented launches only: per-unit timestamp records (8 uint32 per
+  // unit and wave), else nullptr.
+  uint32_t* stamps;
 };
 
 // Launch with at most `grid_cap` persistent workgroups; 0 on success.
 // slab_in: q, k, v are [P][B][S/P][H][D] (sequence-sharded) instead of
-// [B][H][S][D]; only with StoreMode::Slab.
+// [B][H][S][D]; only with StoreMode::Slab.  instr: 0 for the product
+// kernels; for the timestamped instances (D = 128, slab output, c > 0,
+// [B][H][S][D] inputs, p.stamps set) the tile boundary: 1 piggybacked (as
+// the product kernels), 2 completion-coupled, 3 stores then prologue with
+// one wait for both.
 int launch_fwd(int D, StoreMode mode, Variant var, const FwdParams& p, int grid_cap,
-               hipStream_t stream, bool slab_in = false);
+               hipStream_t stream, bool slab_in = false, int instr = 0);
 // Resident workgroups per CU for the instance (D, mode, var); 0 on success.
 int kernel_occupancy(int D, StoreMode mode, Variant var, int* blocks_per_cu);
 

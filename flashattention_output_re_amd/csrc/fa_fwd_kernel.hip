@@ -64,6 +64,11 @@ constexpr float kRaise = 256.0f;   // a lane's stage sum that raises the running
 #endif
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
+// Lambdas of the kernel body are always inlined: one that became a call
+// would take its captures by address, and the unit's buffer resources would
+// then be reloaded from private memory into vector registers.
+#define FA_INL __attribute__((always_inline))
+
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -211,6 +216,10 @@ __device__ __forceinline__ uint32_t dma_lane_off(int wave, int lane, int q) {
 __device__ __forceinline__ void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS DMA has landed
 }
+
+// Wait until every LDS read and write of this wave has completed (lgkmcnt(0);
+// vmcnt and expcnt not waited for).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Wait until at most N of this wave's vector memory operations are in flight
 // (vmcnt(N); expcnt and lgkmcnt not waited for).
@@ -447,40 +456,52 @@ __device__ __forceinline__ void mask_tail(f32x16 (&sc)[2], int stage_key0, int S
       if (key0 + 32 * mb + 8 * (r >> 2) + (r & 3) >= S) sc[mb][r] = fill;
 }
 
-// Epilogue of one wave's 32 queries: normalise by the row sum, round to bf16
-// and store 8 consecutive dims per lane with 128-bit stores, into the slab of
-// the query's destination (Slab) or the [B][H][S][D] output (Plain).  A row
-// whose every key was masked out has l = 0 and stores zeros.
-template <int D, StoreMode MODE>
-__device__ __forceinline__ void store_tile(const FwdParams& p, const f32x16 (&acc)[D / 32],
-                                           float l_run, int qrow, int b, int h, int bh, int g) {
-  constexpr int NDB = D / 32;
-  const float l_tot = halves_sum(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (qrow >= p.S) return;
+// Destination of the stores of lanes whose query row lies past the sequence
+// (rows of a ragged last tile) and of the unused lanes of an instrumented
+// build's timestamp store: written, never read.  Every lane of a storing
+// wave issues every store of the epilogue, so that the wave issues a fixed
+// number of store instructions per unit with no branch around them (the
+// wait at the tile boundary counts them).  64 lanes x D <= 128 bf16.
+__device__ __attribute__((aligned(256))) uint16_t fa_store_sink[64 * 128];
+
+// Epilogue of one wave's 32 queries: scale by inv (1 / the row sum, or 0 for
+// a row whose every key was masked out), round to bf16 and store 8
+// consecutive dims per lane with 128-bit stores, into the slab of the query's
+// destination (Slab) or the [B][H][S][D] output (Plain).  The NDBS 32-dim
+// blocks of o cover dims [d0, d0 + 32 NDBS).  Exactly 2 NDBS store
+// instructions per wave whatever the rows: a lane whose row is >= S stores
+// into fa_store_sink.
+template <int D, StoreMode MODE, int NDBS>
+__device__ __forceinline__ void store_rows(const FwdParams& p, const f32x16 (&o)[NDBS], float inv,
+                                           int qrow, int d0, int b, int h, int bh, int g,
+                                           int lane) {
+  const int row = qrow < p.S ? qrow : p.S - 1;
   size_t row_off;
   if (MODE == StoreMode::Slab) {
-    const int slab = qrow / p.Sp, t = qrow - slab * p.Sp;
+    const int slab = row / p.Sp, t = row - slab * p.Sp;
     row_off = (((size_t)slab * p.B + b) * p.Sp + t) * p.H + h;
   } else {
-    row_off = (size_t)bh * p.S + qrow;
+    row_off = (size_t)bh * p.S + row;
   }
-  uint16_t* dst = p.out + row_off * D;
+  uint16_t* const dst = qrow < p.S ? p.out + row_off * D + d0 : fa_store_sink + lane * D;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < NDBS; ++db) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int r0 = 8 * hf;
-      const uint32_t a0 = pack_bf16(acc[db][r0 + 0] * inv, acc[db][r0 + 1] * inv);
-      const uint32_t a1 = pack_bf16(acc[db][r0 + 2] * inv, acc[db][r0 + 3] * inv);
-      const uint32_t b0 = pack_bf16(acc[db][r0 + 4] * inv, acc[db][r0 + 5] * inv);
-      const uint32_t b1 = pack_bf16(acc[db][r0 + 6] * inv, acc[db][r0 + 7] * inv);
+      const uint32_t a0 = pack_bf16(o[db][r0 + 0] * inv, o[db][r0 + 1] * inv);
+      const uint32_t a1 = pack_bf16(o[db][r0 + 2] * inv, o[db][r0 + 3] * inv);
+      const uint32_t b0 = pack_bf16(o[db][r0 + 4] * inv, o[db][r0 + 5] * inv);
+      const uint32_t b1 = pack_bf16(o[db][r0 + 6] * inv, o[db][r0 + 7] * inv);
       const Pair x = swap_halves(a0, b0);
       const Pair y = swap_halves(a1, b1);
       *reinterpret_cast<u32x4*>(dst + 32 * db + 16 * hf + 8 * g) = u32x4{x.lo, y.lo, x.hi, y.hi};
     }
   }
 }
+
+// Low 32 bits of the shader clock counter.
+__device__ __forceinline__ uint32_t clock_lo() { return (uint32_t)__builtin_amdgcn_s_memtime(); }
 
 // Ping-pong kernel: 8 waves, one workgroup per CU.
 // Waves 0-3 form group 0 and waves 4-7 group 1; the SIMD that runs wave w
@@ -517,8 +538,9 @@ __device__ __forceinline__ void store_tile(const FwdParams& p, const f32x16 (&ac
 // hold the same queries and each computes on, and loads, its own K/V stream
 // with two buffers per tensor: in S(n), K stage n + 2 into the slot of K
 // stage n and V stage n + 1 into the slot of V stage n - 1 (both last read in
-// M(n - 1)), both first read in M(n + 1).  At the end group 1 hands its
-// partial (max, sum, O) to group 0 through LDS, which merges and stores.
+// M(n - 1)), both first read in M(n + 1).  At the end the groups exchange
+// their partial (max, sum, O) through LDS; each merges and stores half of the
+// dims.
 //
 // Masked units (MASKED = true, split-key) are the 128-query tiles of a block
 // mask: the row's K kept 128-key tiles give 2K stages in key order, group 0
@@ -530,11 +552,43 @@ __device__ __forceinline__ void store_tile(const FwdParams& p, const f32x16 (&ac
 // read the tile's head straight from the slabs (slab_row, slab_dma); the
 // arithmetic is unchanged, so the result equals that of [B][H][S][D] inputs
 // bit for bit.
-template <int D, StoreMode MODE, bool NEG, bool SPLIT, bool MASKED = false, bool SLAB_IN = false>
+//
+// Tile boundary (the piggyback).  When a unit's Q-loop is over, each wave
+// first issues the next unit's prologue -- its Q fragments and the first K/V
+// stages of its stream -- then the finished unit's slab stores, and then
+// waits for the prologue only.  gfx950 counts vector loads and stores on one
+// counter, vmcnt, which retires in issue order: vmcnt(N), N = the vector
+// memory instructions issued after the prologue (the stores), completes every
+// older load and leaves the stores in flight.  So the next unit's Q-loop
+// starts while the stores drain.  Its first stages need no DMA wait at all
+// (their data came with the prologue): none in S(0) and S(1) of a whole unit
+// and in S(0) of a split unit.  The first wait that covers the stores is the
+// one for the first refill issued after them, at the end of S(2) (whole) or
+// S(1) (split), two or one stages into the next Q-loop.  Every wave issues the
+// same number of stores per unit (2 NDB whole; NDB split, the two groups
+// storing half of the dims each) with no branch around them, rows >= S going
+// to fa_store_sink, so the count is exact.
+//
+// INSTR (instrumented instances, slab output, D = 128): 1 runs the kernel as
+// above and writes one record of eight uint32 per unit and wave to p.stamps
+// (index (unit * 8 + wave) * 8): the low 32 bits of the shader clock when the
+// wait before the unit's Q-loop returned, after the barrier that starts it,
+// when its last stage was done, when its last store instruction was issued,
+// when those stores were complete (INSTR 2 only, else 0), then the unit, the
+// workgroup and the high 32 bits of the clock at the store issue.  2 is the
+// completion-coupled counterfactual the pages contrast with piggybacking:
+// the owner issues its stores, waits for them to complete (vmcnt(0)), and
+// only then issues the next unit's prologue.  3 keeps the order in which the
+// stores come first and the next unit's prologue second, with one wait for
+// both (so the next Q-loop waits for the stores as well, though their drain
+// overlaps the prologue's loads).
+template <int D, StoreMode MODE, bool NEG, bool SPLIT, bool MASKED = false, bool SLAB_IN = false,
+          int INSTR = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_pp_kernel(FwdParams p) {
   static_assert(!MASKED || SPLIT, "masked units are split-key units");
+  static_assert(INSTR == 0 || (MODE == StoreMode::Slab && D == 128), "instrumented instances");
   constexpr int NKS = D / 16;     // QK^T contraction steps
   constexpr int NDB = D / 32;     // 32-dim blocks of O^T
   constexpr int NA = 2 * NKS;     // QK^T MFMAs per stage
@@ -547,15 +601,17 @@ void fa_fwd_pp_kernel(FwdParams p) {
   // last two regions' worth (whole units issue PW per region, split units
   // 2 PW, and wait for the older of two regions or for the previous one).
   constexpr int NDMA = 2 * PW;
+  constexpr bool COUPLED = INSTR == 2;
+  constexpr bool LATE = INSTR == 3;   // stores, then the next prologue, one wait for both
   // Buffer [i][e] of stream i; one object per (tensor, slot) so that the
   // compiler can tell a DMA into one buffer from reads of another.
   __shared__ __attribute__((aligned(16))) uint16_t kb0[NG][E];
   __shared__ __attribute__((aligned(16))) uint16_t kb1[NG][E];
-  __shared__ __attribute__((aligned(16))) uint16_t kb2[NBUF >= 3 ? NG : 1][NBUF >= 3 ? E : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t kb2[NBUF == 4 ? NG : 1][NBUF == 4 ? E : 8];
   __shared__ __attribute__((aligned(16))) uint16_t kb3[NBUF == 4 ? NG : 1][NBUF == 4 ? E : 8];
   __shared__ __attribute__((aligned(16))) uint16_t vb0[NG][E];
   __shared__ __attribute__((aligned(16))) uint16_t vb1[NG][E];
-  __shared__ __attribute__((aligned(16))) uint16_t vb2[NBUF >= 3 ? NG : 1][NBUF >= 3 ? E : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vb2[NBUF == 4 ? NG : 1][NBUF == 4 ? E : 8];
   __shared__ __attribute__((aligned(16))) uint16_t vb3[NBUF == 4 ? NG : 1][NBUF == 4 ? E : 8];
   // Group 1's running (max, sum) hand-over (split units only).
   __shared__ float ml[SPLIT ? 2 * 256 : 1];
@@ -573,18 +629,18 @@ void fa_fwd_pp_kernel(FwdParams p) {
   const int own = SPLIT ? grp : 0;   // the stream this wave computes on and (SPLIT) loads
   // Stage j of this wave's stream starts at key key_of(j); a stage past the
   // end is read at key S, which the buffer returns as zeros.
-  auto key_of = [&](int j) {
+  auto key_of = [&](int j) FA_INL {
     const int st = own * nsh + j;
     return st < ns ? st * BN : p.S;
   };
   // Stage j of the stream sits in kbuf(j % NBUF) / vbuf(j % NBUF).
-  auto kbuf = [&](int slot) -> uint16_t* {
-    if (NBUF >= 3 && slot == 2) return kb2[own];
+  auto kbuf = [&](int slot) FA_INL -> uint16_t* {
+    if (NBUF == 4 && slot == 2) return kb2[own];
     if (NBUF == 4 && slot == 3) return kb3[own];
     return slot ? kb1[own] : kb0[own];
   };
-  auto vbuf = [&](int slot) -> uint16_t* {
-    if (NBUF >= 3 && slot == 2) return vb2[own];
+  auto vbuf = [&](int slot) FA_INL -> uint16_t* {
+    if (NBUF == 4 && slot == 2) return vb2[own];
     if (NBUF == 4 && slot == 3) return vb3[own];
     return slot ? vb1[own] : vb0[own];
   };
@@ -617,143 +673,321 @@ void fa_fwd_pp_kernel(FwdParams p) {
     }
   }
 
-  // Dense units in XCD-aware order.  Masked units keep the plain order: on a
-  // 30%-dense block mask the XCD-aware order measured slower (its workgroups
-  // skip different tiles, so they do not stream K/V in step as dense tiles
-  // do).
-  const int slot_id = MASKED ? (int)blockIdx.x : xcd_slot(blockIdx.x, gridDim.x);
-  for (int base = 0; base + slot_id < p.units; base += gridDim.x) {
-    const int unit = base + slot_id;
-    // Dense: 256-query tile `tile` (split units: its half unit & 1).  Masked:
-    // 128-query tile qt of head bh, which is mask row qt.
+  // A work unit: dense, 256-query tile `tile` (split units: its half
+  // unit & 1); masked, 128-query tile qt of head bh, which is mask row qt.
+  // [B][H][S][D] inputs: one buffer resource per head slice.  Slab inputs:
+  // one per tensor, with the head's columns at head_col of every row.
+  struct Unit {
+    int bh, qt, b, h, qrow;
+    uint32_t head_col;
+    __amdgpu_buffer_rsrc_t rq, rk, rv;
+  };
+  auto make_unit = [&](int unit) FA_INL {
+    Unit u;
     const int tile = MASKED ? unit : SPLIT ? p.unit_base + (unit >> 1) : unit;
-    const int bh = tile / p.nqt, qt = tile - bh * p.nqt;
-    const int b = bh / p.H, h = bh - b * p.H;
-    // [B][H][S][D] inputs: one resource per head slice.  Slab inputs: one per
-    // tensor, with the head's columns at head_col of every row.
-    const size_t head_off = SLAB_IN ? 0 : (size_t)bh * p.S * D;
+    u.bh = tile / p.nqt;
+    u.qt = tile - u.bh * p.nqt;
+    u.b = u.bh / p.H;
+    u.h = u.bh - u.b * p.H;
+    const size_t head_off = SLAB_IN ? 0 : (size_t)u.bh * p.S * D;
     const uint32_t in_size = SLAB_IN ? in_bytes : head_bytes;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head_off, in_size);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head_off, in_size);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head_off, in_size);
-    const uint32_t head_col = (uint32_t)h * D * 2;
-    // Slab inputs: byte offset of the row of token s < S of this (b, h).
-    auto slab_row = [&](uint32_t s) {
-      const uint32_t ps = (__umulhi(s, p.sp_magic) + s) >> p.sp_shift;
-      return ((ps * p.B + b) * p.Sp + (s - ps * p.Sp)) * rowstride + head_col;
-    };
-    // Slab inputs: this wave's share of the stage that starts at key `key`
-    // into `dst`, lane offsets `lo` within the stage's first slab.  A stage
-    // that runs past the end of a slab continues in the next slab, (B - 1) Sp
-    // rows further on (Sp >= 64, so at most one boundary); keys >= S land
-    // past the tensor and read as zeros.
-    auto slab_dma = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo, int key) {
-      if (key >= p.S) {
-        dma_blocks<PW>(dst, r, in_bytes, lo);
-        return;
-      }
-      const uint32_t ps = (__umulhi((uint32_t)key, p.sp_magic) + key) >> p.sp_shift;
-      const uint32_t base = ((ps * p.B + b) * p.Sp + (key - ps * p.Sp)) * rowstride + head_col;
-      const int left = (int)((ps + 1) * p.Sp) - key;    // rows before the boundary
-      if (left >= BN) {
-        dma_blocks<PW>(dst, r, base, lo);
-        return;
-      }
-      const uint32_t delta = (uint32_t)(p.B - 1) * p.Sp * rowstride;
-      uint32_t o[PW];
+    u.rq = make_rsrc(p.q + head_off, in_size);
+    u.rk = make_rsrc(p.k + head_off, in_size);
+    u.rv = make_rsrc(p.v + head_off, in_size);
+    u.head_col = (uint32_t)u.h * D * 2;
+    u.qrow = MASKED  ? u.qt * BM + wq * 32 + l32
+             : SPLIT ? u.qt * 256 + (unit & 1) * 128 + wq * 32 + l32
+                     : u.qt * 256 + wave * 32 + l32;
+    return u;
+  };
+  // Slab inputs: byte offset of the row of token s < S of unit u's (b, h).
+  auto slab_row = [&](const Unit& u, uint32_t s) FA_INL {
+    const uint32_t ps = (__umulhi(s, p.sp_magic) + s) >> p.sp_shift;
+    return ((ps * p.B + u.b) * p.Sp + (s - ps * p.Sp)) * rowstride + u.head_col;
+  };
+  // Slab inputs: this wave's share of the stage that starts at key `key`
+  // into `dst`, lane offsets `lo` within the stage's first slab.  A stage
+  // that runs past the end of a slab continues in the next slab, (B - 1) Sp
+  // rows further on (Sp >= 64, so at most one boundary); keys >= S land
+  // past the tensor and read as zeros.
+  auto slab_dma = [&](const Unit& u, uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo,
+                      int key) FA_INL {
+    if (key >= p.S) {
+      dma_blocks<PW>(dst, r, in_bytes, lo);
+      return;
+    }
+    const uint32_t ps = (__umulhi((uint32_t)key, p.sp_magic) + key) >> p.sp_shift;
+    const uint32_t base = ((ps * p.B + u.b) * p.Sp + (key - ps * p.Sp)) * rowstride + u.head_col;
+    const int left = (int)((ps + 1) * p.Sp) - key;    // rows before the boundary
+    if (left >= BN) {
+      dma_blocks<PW>(dst, r, base, lo);
+      return;
+    }
+    const uint32_t delta = (uint32_t)(p.B - 1) * p.Sp * rowstride;
+    uint32_t o[PW];
 #pragma unroll
-      for (int q = 0; q < PW; ++q) o[q] = lo[q] + (row0 + q * (64 / Tile<D>::CH) >= left ? delta : 0u);
-      dma_blocks<PW>(dst, r, base, o);
-    };
-    // The same share as a DmaPlan ([B][H][S][D] inputs): instruction q reads
-    // the byte offsets dma_blocks would use.
-    auto plan_of = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo, int key) {
-      DmaPlan<PW> pl;
-      pl.lds = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
-      pl.r = r;
+    for (int q = 0; q < PW; ++q) o[q] = lo[q] + (row0 + q * (64 / Tile<D>::CH) >= left ? delta : 0u);
+    dma_blocks<PW>(dst, r, base, o);
+  };
+  // The same share as a DmaPlan ([B][H][S][D] inputs): instruction q reads
+  // the byte offsets dma_blocks would use.
+  auto plan_of = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo, int key) FA_INL {
+    DmaPlan<PW> pl;
+    pl.lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
+    pl.r = r;
 #pragma unroll
-      for (int q = 0; q < PW; ++q) pl.addr[q] = (uint32_t)key * (D * 2) + lo[q];
-      return pl;
-    };
-    // Masked units: this group's stream of kept stages, and the first keys of
-    // stages n, n + 1 and n + 2 of the stream (key_n[0..2]), advanced after
-    // each stage.
-    KeptStages kept;
-    int key_n[3] = {0, 0, 0};
-    int nloop = SPLIT ? nsh : ns;
-    if (MASKED) {
-      nloop = kept.init(p.mask + ((size_t)h * p.nmt + qt) * p.mw, p.nmt, p.mw, p.S, own);
+    for (int q = 0; q < PW; ++q) pl.addr[q] = (uint32_t)key * (D * 2) + lo[q];
+    return pl;
+  };
+  // Masked units: this group's stream of kept stages, and the first keys of
+  // stages n, n + 1 and n + 2 of the stream (key_n[0..2]), advanced after
+  // each stage.  nloop: the stages of this wave's stream in the unit.
+  KeptStages kept;
+  int key_n[3] = {0, 0, 0};
+  int nloop = SPLIT ? nsh : ns;
+  auto start_stream = [&](const Unit& u) FA_INL {
+    if constexpr (MASKED) {
+      nloop = kept.init(p.mask + ((size_t)u.h * p.nmt + u.qt) * p.mw, p.nmt, p.mw, p.S, own);
       key_n[0] = kept.next();
       key_n[1] = kept.next();
       key_n[2] = kept.next();
     }
-    // First key of stage j of this wave's stream.
-    auto stage_key = [&](int j) { return MASKED ? key_n[j] : key_of(j); };
-    // This wave's share of the K or V stage that starts at key `key` into slot `slot`.
-    auto dma_k = [&](int slot, int key) {
-      if constexpr (SLAB_IN) {
-        slab_dma(kbuf(slot) + 64 * 8 * PW * wq, rk, koff, key);
-      } else {
-        dma_blocks<PW>(kbuf(slot) + 64 * 8 * PW * wq, rk, (uint32_t)key * (D * 2), koff);
-      }
-    };
-    auto dma_v = [&](int slot, int key) {
-      if constexpr (SLAB_IN) {
-        slab_dma(vbuf(slot) + 64 * 8 * PW * wq, rv, SPLIT ? voff : koff, key);
-      } else {
-        dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, rv, (uint32_t)key * (D * 2), SPLIT ? voff : koff);
-      }
-    };
-    // The DMA issued in region S(n) (SLOT = n % NBUF), after the barrier
-    // that ends every wave's reads of the slots it refills: at the region's
-    // start, except that split units with [B][H][S][D] inputs spread theirs
-    // over four points of the softmax (split_plans; measured faster there,
-    // slower for whole units and for slab inputs, whose per-lane slab
-    // addresses would then stay live through the softmax).
-    // Whole units: K stage n + 3 (group 0) or V stage n + 3 (group 1) into
-    // the slot that stage n - 1 freed.  Split units, each group on its own
-    // stream: K stage n + 2 into the slot of K stage n (read in M(n - 1)) and
-    // V stage n + 1 into the slot of V stage n - 1 (read in M(n - 1)).
-    auto stage_dma = [&](auto SLOT, int n) {
-      constexpr int slot = decltype(SLOT)::value;
-      if (SPLIT) {
-        dma_k(slot, MASKED ? key_n[2] : key_of(n + 2));
-        dma_v((slot + 1) % NBUF, MASKED ? key_n[1] : key_of(n + 1));
-      } else if constexpr (!SLAB_IN) {
-        // One code path for both groups (the tensor and slot selected, not
-        // branched on): the softmax wave takes no branch to issue its DMA.
-        constexpr int sl = (slot + 3) % NBUF;
-        uint16_t* const dst = (grp == 0 ? kbuf(sl) : vbuf(sl)) + 64 * 8 * PW * wq;
-        dma_blocks<PW>(dst, grp == 0 ? rk : rv, (uint32_t)key_of(n + 3) * (D * 2), koff);
-      } else if (grp == 0) {
-        dma_k((slot + 3) % NBUF, key_of(n + 3));
-      } else {
-        dma_v((slot + 3) % NBUF, key_of(n + 3));
-      }
+  };
+  // First key of stage j of this wave's stream.
+  auto stage_key = [&](int j) FA_INL { return MASKED ? key_n[j] : key_of(j); };
+  // This wave's share of unit u's K or V stage that starts at key `key`
+  // into slot `slot`.
+  auto dma_k = [&](const Unit& u, int slot, int key) FA_INL {
+    if constexpr (SLAB_IN) {
+      slab_dma(u, kbuf(slot) + 64 * 8 * PW * wq, u.rk, koff, key);
+    } else {
+      dma_blocks<PW>(kbuf(slot) + 64 * 8 * PW * wq, u.rk, (uint32_t)key * (D * 2), koff);
+    }
+  };
+  auto dma_v = [&](const Unit& u, int slot, int key) FA_INL {
+    if constexpr (SLAB_IN) {
+      slab_dma(u, vbuf(slot) + 64 * 8 * PW * wq, u.rv, SPLIT ? voff : koff, key);
+    } else {
+      dma_blocks<PW>(vbuf(slot) + 64 * 8 * PW * wq, u.rv, (uint32_t)key * (D * 2),
+                     SPLIT ? voff : koff);
+    }
+  };
 
-    };
-    // Split units, [B][H][S][D] inputs: the same stages as DmaPlans, issued
-    // during the softmax.
-    struct SplitPlans { DmaPlan<PW> k, v; };
-    auto split_plans = [&](auto SLOT, int n) {
-      constexpr int slot = decltype(SLOT)::value;
-      const int wofs = 64 * 8 * PW * wq;
-      return SplitPlans{plan_of(kbuf(slot) + wofs, rk, koff, MASKED ? key_n[2] : key_of(n + 2)),
-                        plan_of(vbuf((slot + 1) % NBUF) + wofs, rv, voff, MASKED ? key_n[1] : key_of(n + 1))};
-    };
+  Unit cur;                 // the unit whose Q-loop runs
+  bf16x8 qf[NKS];           // its Q fragments
+  f32x16 s[2];              // the score tile of the current stage
+  f32x16 acc[NDB];          // O^T accumulator
+  float m_run = 0.0f, l_run = 0.0f;
 
-    const int qrow = MASKED  ? qt * BM + wq * 32 + l32
-                     : SPLIT ? qt * 256 + (unit & 1) * 128 + wq * 32 + l32
-                             : qt * 256 + wave * 32 + l32;
-    const uint32_t qbase = !SLAB_IN ? (uint32_t)(qrow * D * 2)
-                           : qrow < p.S ? slab_row((uint32_t)qrow) : in_bytes;
-    bf16x8 qf[NKS];
+  // Prologue of unit u: the Q fragments and the first K/V stages of this
+  // wave's stream -- K stages 0 and 1 and V stage 0 (SPLIT: each group, its
+  // own stream) or K stages 0-2 (group 0) and V stages 0-2 (group 1).
+  auto prologue = [&](const Unit& u) FA_INL {
+    const uint32_t qbase = !SLAB_IN ? (uint32_t)(u.qrow * D * 2)
+                           : u.qrow < p.S ? slab_row(u, (uint32_t)u.qrow) : in_bytes;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, load16(rq, qbase + ks * 32 + g * 16));
+      qf[ks] = __builtin_bit_cast(bf16x8, load16(u.rq, qbase + ks * 32 + g * 16));
+    if (SPLIT || grp == 0) {
+      dma_k(u, 0, stage_key(0));
+      dma_k(u, 1, stage_key(1));
+    }
+    if (!SPLIT && grp == 0) dma_k(u, 2, key_of(2));
+    if (SPLIT) {
+      dma_v(u, 0, stage_key(0));
+    } else if (grp == 1) {
+      dma_v(u, 0, stage_key(0));
+      dma_v(u, 1, stage_key(1));
+      dma_v(u, 2, key_of(2));
+    }
+  };
 
-    f32x16 acc[NDB];
+  // The DMA issued in region S(n) (SLOT = n % NBUF), after the barrier
+  // that ends every wave's reads of the slots it refills: at the region's
+  // start, except that split units with [B][H][S][D] inputs spread theirs
+  // over four points of the softmax (split_plans; measured faster there,
+  // slower for whole units and for slab inputs, whose per-lane slab
+  // addresses would then stay live through the softmax).
+  // Whole units: K stage n + 3 (group 0) or V stage n + 3 (group 1) into
+  // the slot that stage n - 1 freed.  Split units, each group on its own
+  // stream: K stage n + 2 into the slot of K stage n (read in M(n - 1)) and
+  // V stage n + 1 into the slot of V stage n - 1 (read in M(n - 1)).
+  auto stage_dma = [&](auto SLOT, int n) FA_INL {
+    constexpr int slot = decltype(SLOT)::value;
+    if (SPLIT) {
+      dma_k(cur, slot, MASKED ? key_n[2] : key_of(n + 2));
+      dma_v(cur, (slot + 1) % NBUF, MASKED ? key_n[1] : key_of(n + 1));
+    } else if constexpr (!SLAB_IN) {
+      // One code path for both groups (the tensor and slot selected, not
+      // branched on): the softmax wave takes no branch to issue its DMA.
+      constexpr int sl = (slot + 3) % NBUF;
+      uint16_t* const dst = (grp == 0 ? kbuf(sl) : vbuf(sl)) + 64 * 8 * PW * wq;
+      dma_blocks<PW>(dst, grp == 0 ? cur.rk : cur.rv, (uint32_t)key_of(n + 3) * (D * 2), koff);
+    } else if (grp == 0) {
+      dma_k(cur, (slot + 3) % NBUF, key_of(n + 3));
+    } else {
+      dma_v(cur, (slot + 3) % NBUF, key_of(n + 3));
+    }
+  };
+  // Split units, [B][H][S][D] inputs: the same stages as DmaPlans, issued
+  // during the softmax.
+  struct SplitPlans { DmaPlan<PW> k, v; };
+  auto split_plans = [&](auto SLOT, int n) FA_INL {
+    constexpr int slot = decltype(SLOT)::value;
+    const int wofs = 64 * 8 * PW * wq;
+    return SplitPlans{plan_of(kbuf(slot) + wofs, cur.rk, koff, MASKED ? key_n[2] : key_of(n + 2)),
+                      plan_of(vbuf((slot + 1) % NBUF) + wofs, cur.rv, voff,
+                              MASKED ? key_n[1] : key_of(n + 1))};
+  };
+
+  // Region S(n), SLOT = n % NBUF: this wave's DMA, the softmax of stage n,
+  // then the wait that completes this wave's DMA from S(n - 2) (split
+  // units: S(n - 1)) before the barrier that precedes its first readers.
+  // The first stages of a unit need no wait (their stages came with the
+  // prologue, which the tile boundary waited for): S(0) and S(1) of a whole
+  // unit, S(0) of a split unit.
+  auto region_s = [&](auto SLOT, int n, StageProbs<NEG>& sm) FA_INL {
+    const int key0 = MASKED ? key_n[0] : (own * nsh + n) * BN;
+    if constexpr (SPLIT && !SLAB_IN) {
+      const SplitPlans pl = split_plans(SLOT, n);
+      mask_tail(s, key0, p.S, g, fill);
+      sm.template compute<true>(s, c, m_run, l_run, [&](int j) {
+        constexpr int STEP = 4 / PW;
+        if (j % STEP == 0) {
+          pl.k.issue(j / STEP);
+          pl.v.issue(j / STEP);
+        }
+      });
+    } else {
+      stage_dma(SLOT, n);
+      mask_tail(s, key0, p.S, g, fill);
+      sm.template compute<false>(s, c, m_run, l_run, [](int) {});
+    }
+    if (n >= (SPLIT ? 1 : 2)) wait_vm<NDMA>();
+  };
+  // Region M(n): the scores of stage n + 1 (K stage n + 1) and PV of stage
+  // n (V stage n).  After the last stage the QK^T MFMAs read a buffer of
+  // zeros and their result is unused.
+  auto region_m = [&](auto SLOT, const StageProbs<NEG>& sm) FA_INL {
+    constexpr int slot = decltype(SLOT)::value;
+    // Raised wave priority while this wave issues MFMAs: when both waves
+    // of a SIMD have an instruction ready, the matrix core's feeder goes
+    // first and the softmax wave's VALU work fills the gaps.
+    __builtin_amdgcn_s_setprio(2);
+    const uint16_t* const kn = kbuf((slot + 1) % NBUF);
+    const uint16_t* const vt = vbuf(slot);
+    if (__builtin_expect(sm.rescale, 0)) {   // rare: out of line
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= sm.alpha;
+    }
+    static_assert(NA == NB, "one QK^T MFMA per PV MFMA");
+    constexpr int LEAD = FA_MLEAD;
+    auto ka_read = [&](int i) FA_INL { return k_operand<D>(kn, i & 1, i >> 1, l32, g); };
+    auto va_read = [&](int j) FA_INL { return v_operand<D>(vt, j / NDB, j % NDB, lane); };
+    // Whole units interleave the two products, QK^T MFMA i before PV MFMA
+    // i; split units issue all of QK^T first, then PV.  Each accumulator
+    // sees the same operands in the same order either way (the results
+    // are bit-identical); these orders measured fastest for each form.
+    auto qk = [&](int i, const bf16x8& a) FA_INL {
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i >> 1],
+                                                         i < 2 ? f32x16{} : s[i & 1], 0, 0, 0);
+    };
+    auto pv = [&](int j, const bf16x8& a) FA_INL {
+      acc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sm.p_operand(j / NDB),
+                                                             acc[j % NDB], 0, 0, 0);
+    };
+    if constexpr (!SPLIT) {
+      bf16x8 ka[NA], va[NB];
+#pragma unroll
+      for (int i = 0; i < LEAD; ++i) {
+        va[i] = va_read(i);
+        ka[i] = ka_read(i);
+      }
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        if (i + LEAD < NA) {
+          va[i + LEAD] = va_read(i + LEAD);
+          ka[i + LEAD] = ka_read(i + LEAD);
+        }
+        qk(i, ka[i]);
+        pv(i, va[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // Operand t: QK^T MFMA t (t < NA) or PV MFMA t - NA, read 2 LEAD ahead.
+      bf16x8 op[NA + NB];
+      auto rd = [&](int t) FA_INL { op[t] = t < NA ? ka_read(t) : va_read(t - NA); };
+#pragma unroll
+      for (int t = 0; t < 2 * LEAD; ++t) rd(t);
+#pragma unroll
+      for (int t = 0; t < NA + NB; ++t) {
+        if (t + 2 * LEAD < NA + NB) rd(t + 2 * LEAD);
+        if (t < NA)
+          qk(t, op[t]);
+        else
+          pv(t - NA, op[t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // One stage: S, barrier, M, barrier.
+  auto stage = [&](auto SLOT, int n) FA_INL {
+    StageProbs<NEG> sm;
+    region_s(SLOT, n, sm);
+    barrier_keep_dma();
+    region_m(SLOT, sm);
+    // Masked units advance their stream's stage keys here, at the end of
+    // the MFMA region, rather than at the start of the next softmax region:
+    // the scalar mask walk then costs the MFMA wave (whose operand reads
+    // are all consumed by now) instead of the softmax wave.
+    if (MASKED) {
+      key_n[0] = key_n[1];
+      key_n[1] = key_n[2];
+      key_n[2] = kept.next();
+    }
+    barrier_keep_dma();
+  };
+  // A unit's stages.
+  auto stages = [&]() FA_INL {
+    for (int n = 0; n < nloop; n += NBUF) {
+      stage(std::integral_constant<int, 0>{}, n);
+      if (n + 1 >= nloop) break;
+      stage(std::integral_constant<int, 1>{}, n + 1);
+      if constexpr (NBUF == 4) {
+        if (n + 2 >= nloop) break;
+        stage(std::integral_constant<int, 2>{}, n + 2);
+        if (n + 3 >= nloop) break;
+        stage(std::integral_constant<int, 3>{}, n + 3);
+      }
+    }
+  };
+
+  // Dense units in XCD-aware order.  Masked units keep the plain order: on a
+  // 30%-dense block mask the XCD-aware order measured slower (its workgroups
+  // skip different tiles, so they do not stream K/V in step as dense tiles
+  // do).
+  int unit = MASKED ? (int)blockIdx.x : xcd_slot(blockIdx.x, gridDim.x);
+  if (unit >= p.units) return;
+  cur = make_unit(unit);
+  start_stream(cur);
+  prologue(cur);
+  wait_vm<0>();
+  uint32_t t_ready = INSTR ? clock_lo() : 0u;
+  for (;;) {
+    // Every wave's prologue DMA has landed; every wave computes the scores of
+    // its stream's first stage.
+    barrier_keep_dma();
+    const uint32_t t_start = INSTR ? clock_lo() : 0u;
+    qk_mfma<D>(s, kbuf(0), qf, l32, g);
+    // Every read of K stage 0 has returned before the barrier (split units
+    // refill its slot in S(0)).
+    wait_lds();
+    barrier_keep_dma();
+    if (grp == 1) barrier_keep_dma();   // group 1 starts one region behind
 #pragma unroll
     for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
     // A finite starting max: the first stage's probabilities overflow against
@@ -761,195 +995,110 @@ void fa_fwd_pp_kernel(FwdParams p) {
     // while keys past the end (fill, -inf after scaling) and a masked stream's
     // stage with no key at all (the second half of a kept last tile shorter
     // than 64 keys) weigh exp2(-inf) = 0 rather than NaN.
-    float m_run = -3.0e38f;
+    m_run = -3.0e38f;
+    l_run = 0.0f;
 
-    float l_run = 0.0f;
+    stages();
 
-    // Prologue: K stages 0 and 1 and V stage 0 (SPLIT: each group, its own
-    // stream) or K stages 0-2 (group 0) and V stages 0-2 (group 1); every
-    // wave computes the scores of its stream's first stage.
-    if (SPLIT || grp == 0) {
-      dma_k(0, stage_key(0));
-      dma_k(1, stage_key(1));
-    }
-    if (!SPLIT && grp == 0) dma_k(2, key_of(2));
-    if (SPLIT) {
-      dma_v(0, stage_key(0));
-    } else if (grp == 1) {
-      dma_v(0, stage_key(0));
-      dma_v(1, stage_key(1));
-      dma_v(2, key_of(2));
-    }
-    wait_dma();
-    __syncthreads();
-    f32x16 s[2];
-    qk_mfma<D>(s, kbuf(0), qf, l32, g);
-    __syncthreads();
-    if (grp == 1) __syncthreads();   // group 1 starts one region behind
-
-    // Region S(n), SLOT = n % NBUF: this wave's DMA, the softmax of stage n,
-    // then the wait that completes this wave's DMA from S(n - 2) (split
-    // units: S(n - 1)) before the barrier that precedes its first readers.
-    auto region_s = [&](auto SLOT, int n, StageProbs<NEG>& sm) {
-      const int key0 = MASKED ? key_n[0] : (own * nsh + n) * BN;
-      if constexpr (SPLIT && !SLAB_IN) {
-        const SplitPlans pl = split_plans(SLOT, n);
-        mask_tail(s, key0, p.S, g, fill);
-        sm.template compute<true>(s, c, m_run, l_run, [&](int j) {
-          constexpr int STEP = 4 / PW;
-          if (j % STEP == 0) {
-            pl.k.issue(j / STEP);
-            pl.v.issue(j / STEP);
-          }
-        });
-      } else {
-        stage_dma(SLOT, n);
-        mask_tail(s, key0, p.S, g, fill);
-        sm.template compute<false>(s, c, m_run, l_run, [](int) {});
-      }
-      wait_vm<NDMA>();
-    };
-    // Region M(n): the scores of stage n + 1 (K stage n + 1) and PV of stage
-    // n (V stage n).  After the last stage the QK^T MFMAs read a buffer of
-    // zeros and their result is unused.
-    auto region_m = [&](auto SLOT, const StageProbs<NEG>& sm) {
-      constexpr int slot = decltype(SLOT)::value;
-      // Raised wave priority while this wave issues MFMAs: when both waves
-      // of a SIMD have an instruction ready, the matrix core's feeder goes
-      // first and the softmax wave's VALU work fills the gaps.
-      __builtin_amdgcn_s_setprio(2);
-      const uint16_t* const kn = kbuf((slot + 1) % NBUF);
-      const uint16_t* const vt = vbuf(slot);
-      if (__builtin_expect(sm.rescale, 0)) {   // rare: out of line
-#pragma unroll
-        for (int i = 0; i < NDB; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][r] *= sm.alpha;
-      }
-      static_assert(NA == NB, "one QK^T MFMA per PV MFMA");
-      constexpr int LEAD = FA_MLEAD;
-      auto ka_read = [&](int i) { return k_operand<D>(kn, i & 1, i >> 1, l32, g); };
-      auto va_read = [&](int j) { return v_operand<D>(vt, j / NDB, j % NDB, lane); };
-      // Whole units interleave the two products, QK^T MFMA i before PV MFMA
-      // i; split units issue all of QK^T first, then PV.  Each accumulator
-      // sees the same operands in the same order either way (the results
-      // are bit-identical); these orders measured fastest for each form.
-      auto qk = [&](int i, const bf16x8& a) {
-        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i >> 1],
-                                                           i < 2 ? f32x16{} : s[i & 1], 0, 0, 0);
-      };
-      auto pv = [&](int j, const bf16x8& a) {
-        acc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sm.p_operand(j / NDB),
-                                                               acc[j % NDB], 0, 0, 0);
-      };
-      if constexpr (!SPLIT) {
-        bf16x8 ka[NA], va[NB];
-#pragma unroll
-        for (int i = 0; i < LEAD; ++i) {
-          va[i] = va_read(i);
-          ka[i] = ka_read(i);
-        }
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-          if (i + LEAD < NA) {
-            va[i + LEAD] = va_read(i + LEAD);
-            ka[i + LEAD] = ka_read(i + LEAD);
-          }
-          qk(i, ka[i]);
-          pv(i, va[i]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-        // Operand t: QK^T MFMA t (t < NA) or PV MFMA t - NA, read 2 LEAD ahead.
-        bf16x8 op[NA + NB];
-        auto rd = [&](int t) { op[t] = t < NA ? ka_read(t) : va_read(t - NA); };
-#pragma unroll
-        for (int t = 0; t < 2 * LEAD; ++t) rd(t);
-#pragma unroll
-        for (int t = 0; t < NA + NB; ++t) {
-          if (t + 2 * LEAD < NA + NB) rd(t + 2 * LEAD);
-          if (t < NA)
-            qk(t, op[t]);
-          else
-            pv(t - NA, op[t]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    };
-    // One stage: S, barrier, M, barrier.
-    auto stage = [&](auto SLOT, int n) {
-      StageProbs<NEG> sm;
-      region_s(SLOT, n, sm);
-      barrier_keep_dma();
-      region_m(SLOT, sm);
-      // Masked units advance their stream's stage keys here, at the end of
-      // the MFMA region, rather than at the start of the next softmax region:
-      // the scalar mask walk then costs the MFMA wave (whose operand reads
-      // are all consumed by now) instead of the softmax wave.
-      if (MASKED) {
-        key_n[0] = key_n[1];
-        key_n[1] = key_n[2];
-        key_n[2] = kept.next();
-      }
-      barrier_keep_dma();
-    };
-
-
-    for (int n = 0; n < nloop; n += NBUF) {
-      stage(std::integral_constant<int, 0>{}, n);
-      if (n + 1 >= nloop) break;
-      stage(std::integral_constant<int, 1>{}, n + 1);
-      if (NBUF >= 3) {
-        if (n + 2 >= nloop) break;
-        stage(std::integral_constant<int, 2 % NBUF>{}, n + 2);
-      }
-      if (NBUF == 4) {
-        if (n + 3 >= nloop) break;
-        stage(std::integral_constant<int, 3 % NBUF>{}, n + 3);
-      }
-    }
     wait_dma();   // DMA of stages past the end, before the buffers are reused
-
-    // Epilogue.  Group 0's trailing region ends with the barrier that ends
-    // group 1's last M.  In split units group 1 then hands its partial state
-    // over through stream 0's four K/V buffers, idle by now and written only
-    // by group 0 (whose next DMA follows its own reads): wave wq's O^T
-    // accumulator (NDB x 16 floats per lane, one buffer exactly) at float
-    // (db * 16 + r) * 64 + lane of buffer wq, its running max and sum in ml.
+    const uint32_t t_epi = INSTR ? clock_lo() : 0u;
+    // Group 0's trailing region ends with the barrier that ends group 1's
+    // last M: every wave's reads of the K/V buffers are over.
     if (grp == 0) barrier_keep_dma();
-    static_assert(NDB * 16 * 64 * 4 == E * 2, "one buffer per wave");
-    float* const area = reinterpret_cast<float*>(wq == 0 ? kb0[0] : wq == 1 ? kb1[0]
-                                                 : wq == 2 ? vb0[0] : vb1[0]);
+
+    // Split units: group 1 hands its partial state over through stream 0's
+    // four K/V buffers, idle by now: wave wq's O^T accumulator (NDB x 16
+    // floats per lane, one buffer exactly) at float (db * 16 + r) * 64 + lane
+    // of buffer wq, its running max and sum in ml; group 0 merges and stores.
+    if constexpr (SPLIT) {
+      static_assert(NDB * 16 * 64 * 4 == E * 2, "one buffer per wave");
+      float* const area = reinterpret_cast<float*>(wq == 0 ? kb0[0] : wq == 1 ? kb1[0]
+                                                   : wq == 2 ? vb0[0] : vb1[0]);
+      if (grp == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) area[(db * 16 + r) * 64 + lane] = acc[db][r];
+        ml[wq * 64 + lane] = m_run;
+        ml[256 + wq * 64 + lane] = l_run;
+      }
+      __syncthreads();
+      if (grp == 0) {
+        const float m_y = ml[wq * 64 + lane];
+        const float l_y = ml[256 + wq * 64 + lane];
+        const float m = fmaxf(m_run, m_y);
+        const float ax = __builtin_amdgcn_exp2f(m_run - m);
+        const float ay = __builtin_amdgcn_exp2f(m_y - m);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[db][r] = acc[db][r] * ax + area[(db * 16 + r) * 64 + lane] * ay;
+        l_run = l_run * ax + l_y * ay;
+      }
+      // Group 0 has read the hand-over area before the next unit's prologue
+      // refills stream 0's buffers.
+      __syncthreads();
+    }
+    const float l_tot = halves_sum(l_run);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+
+    // The tile boundary: the next unit's prologue, then this unit's stores
+    // (COUPLED: the stores, their completion, then the prologue).
+    const int next = unit + (int)gridDim.x;
+    const bool more = next < p.units;
+    Unit nxt = cur;
+    auto next_prologue = [&]() FA_INL {
+      if (more) {
+        nxt = make_unit(next);
+        start_stream(nxt);
+        prologue(nxt);
+      }
+    };
+    if (!COUPLED && !LATE) next_prologue();
+    // Keep the stores after the prologue's loads.
+    asm volatile("" ::: "memory");
+    // After a wave's NS stores: the timestamps (INSTR), then the wait for
+    // the prologue only, the NS stores (and the record store) staying in
+    // flight; COUPLED: the wait for the stores, the prologue, and the wait
+    // for everything.
+    auto finish = [&](auto NS) FA_INL {
+      constexpr int nst = decltype(NS)::value + (INSTR ? 1 : 0);
+      if constexpr (INSTR) {
+        const uint64_t t = __builtin_amdgcn_s_memtime();
+        uint32_t t_complete = 0;
+        if constexpr (COUPLED) {
+          wait_vm<0>();   // the stores have completed
+          t_complete = clock_lo();
+          next_prologue();
+        }
+        if constexpr (LATE) next_prologue();
+        // Lanes 0 and 1 write the record; the others write the sink.
+        uint32_t* const rec = p.stamps + ((size_t)unit * 8 + wave) * 8;
+        const u32x4 val = lane == 0 ? u32x4{t_ready, t_start, t_epi, (uint32_t)t}
+                                    : u32x4{t_complete, (uint32_t)unit, (uint32_t)blockIdx.x,
+                                            (uint32_t)(t >> 32)};
+        u32x4* const to = lane < 2 ? reinterpret_cast<u32x4*>(rec) + lane
+                                   : reinterpret_cast<u32x4*>(fa_store_sink) + lane;
+        *to = val;
+      }
+      if constexpr (COUPLED || LATE)
+        wait_vm<0>();
+      else
+        wait_vm<nst>();
+    };
+    // Whole units: every wave stores its 32 queries.  Split units: group 0
+    // stores the merged tile, group 1 nothing.
     if (SPLIT && grp == 1) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) area[(db * 16 + r) * 64 + lane] = acc[db][r];
-      ml[wq * 64 + lane] = m_run;
-      ml[256 + wq * 64 + lane] = l_run;
+      finish(std::integral_constant<int, 0>{});
+    } else {
+      store_rows<D, MODE, NDB>(p, acc, inv, cur.qrow, 0, cur.b, cur.h, cur.bh, g, lane);
+      finish(std::integral_constant<int, 2 * NDB>{});
     }
-    __syncthreads();
-    if (SPLIT && grp == 0) {
-      const float m_y = ml[wq * 64 + lane];
-      const float l_y = ml[256 + wq * 64 + lane];
-      const float m = fmaxf(m_run, m_y);
-      const float ax = __builtin_amdgcn_exp2f(m_run - m);
-      const float ay = __builtin_amdgcn_exp2f(m_y - m);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[db][r] = acc[db][r] * ax + area[(db * 16 + r) * 64 + lane] * ay;
-      l_run = l_run * ax + l_y * ay;
-    }
-    // In split units only group 0 stores: group 1 passes its rows as S (past
-    // the end), which store_tile skips.  (A branch around the call instead
-    // makes the register allocator spill.)
-    store_tile<D, MODE>(p, acc, l_run, SPLIT && grp == 1 ? p.S : qrow, b, h, bh, g);
-    // Group 0 has read the hand-over area (stream 0's buffers) before the
-    // next unit's prologue refills them.
-    if (SPLIT) __syncthreads();
+    if constexpr (INSTR) t_ready = clock_lo();
+    if (!more) break;
+    cur = nxt;
+    unit = next;
   }
 }
 
@@ -957,10 +1106,10 @@ void fa_fwd_pp_kernel(FwdParams p) {
 template <Variant VAR> constexpr bool kSplit = VAR != Variant::Whole;
 template <Variant VAR> constexpr bool kMasked = VAR == Variant::Masked;
 
-template <Variant VAR, int D, StoreMode MODE, bool NEG, bool SLAB_IN>
+template <Variant VAR, int D, StoreMode MODE, bool NEG, bool SLAB_IN, int INSTR = 0>
 static int launch_one(const FwdParams& p, int grid_cap, hipStream_t stream) {
   const int grid = p.units < grid_cap ? p.units : grid_cap;
-  hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, kSplit<VAR>, kMasked<VAR>, SLAB_IN>),
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, kSplit<VAR>, kMasked<VAR>, SLAB_IN, INSTR>),
                      dim3(grid), dim3(512), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -1019,9 +1168,31 @@ static int launch_v(int D, StoreMode mode, const FwdParams& p, int grid_cap, hip
                   : launch_d<VAR, 64>(mode, p, grid_cap, stream, slab_in);
 }
 
+// Instrumented instances: D = 128, slab output, c > 0, [B][H][S][D] inputs.
+template <Variant VAR>
+static int launch_instr(int instr, const FwdParams& p, int grid_cap, hipStream_t stream) {
+  switch (instr) {
+    case 1: return launch_one<VAR, 128, StoreMode::Slab, false, false, 1>(p, grid_cap, stream);
+    case 2: return launch_one<VAR, 128, StoreMode::Slab, false, false, 2>(p, grid_cap, stream);
+    case 3: return launch_one<VAR, 128, StoreMode::Slab, false, false, 3>(p, grid_cap, stream);
+  }
+  return -1;
+}
+
 int launch_fwd(int D, StoreMode mode, Variant var, const FwdParams& p, int grid_cap,
-               hipStream_t stream, bool slab_in) {
+               hipStream_t stream, bool slab_in, int instr) {
   if (D != 64 && D != 128) return -1;
+  if (instr != 0) {
+    if (D != 128 || mode != StoreMode::Slab || slab_in || !(p.c > 0.0f) || !p.stamps ||
+        instr < 1 || instr > 3)
+      return -1;
+    switch (var) {
+      case Variant::Whole: return launch_instr<Variant::Whole>(instr, p, grid_cap, stream);
+      case Variant::Split: return launch_instr<Variant::Split>(instr, p, grid_cap, stream);
+      case Variant::Masked: return launch_instr<Variant::Masked>(instr, p, grid_cap, stream);
+    }
+    return -1;
+  }
   switch (var) {
     case Variant::Whole: return launch_v<Variant::Whole>(D, mode, p, grid_cap, stream, slab_in);
     case Variant::Split: return launch_v<Variant::Split>(D, mode, p, grid_cap, stream, slab_in);

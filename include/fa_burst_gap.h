@@ -14,7 +14,9 @@
  *
  * burst_gap_run_async: `producers` workgroups of 256 threads, one per CU
  * (each asks for 96 KiB of LDS so no two share a CU), run `bursts` rounds:
- *   issue bytes_per_producer bytes of 16-byte stores (no wait for completion),
+ *   issue bytes_per_producer bytes of 16-byte stores (no wait for completion;
+ *   coupled = 1: every wave then waits until its stores have completed, the
+ *   completion-coupled issuer the pages contrast with the X-Stage view),
  *   workgroup barrier, then `gap_iters` iterations of a dependent FMA chain
  *   (the compute gap), workgroup barrier.
  * Chunk c (16 bytes) of producer k in burst i lands at byte offset
@@ -30,7 +32,7 @@
  * dst (device) needs bursts * producers * bytes_per_producer bytes, 16-byte
  * aligned; bytes_per_producer is a positive multiple of 4096; producers in
  * [1, 4096]; bursts in [1, 4096]; gap_iters >= 0; nontemporal 0 or 1 selects
- * plain or non-temporal stores.  Returns FA_OK or FA_EINVAL / FA_EALIGN /
+ * plain or non-temporal stores; coupled 0 or 1.  Returns FA_OK or FA_EINVAL / FA_EALIGN /
  * FA_ERANGE (dst larger than 2^40 bytes) / FA_ELAUNCH / FA_EDEVICE, checked
  * before any HIP call.  Caller owns both buffers.
  */
@@ -45,7 +47,7 @@ extern "C" {
 #endif
 
 int burst_gap_run_async(void* dst, uint64_t* times, int producers, int bytes_per_producer,
-                        int bursts, int gap_iters, int nontemporal, void* stream);
+                        int bursts, int gap_iters, int nontemporal, int coupled, void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,12 +40,15 @@ def lib():
 
 
 def test_every_declared_symbol_is_exported(lib):
-    names = declared_functions()
-    other = os.path.join(ROOT, "include", "fa_burst_gap.h")   # the microbenchmark's header
-    with open(other) as f:
-        extra = re.findall(r"^\s*int\s+(\w+)\s*\(", re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S),
-                           re.M)
-    assert set(names) | set(extra) == set(binding.SIGNATURES), names
+    """Every function declared in include/*.h is exported and bound, and the
+    binding binds nothing else."""
+    import glob
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        with open(path) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, re.M))
+    assert names == set(binding.SIGNATURES), sorted(names ^ set(binding.SIGNATURES))
     for n in names:
         assert hasattr(lib, n), n
 
@@ -79,6 +82,7 @@ def _plain(lib, q=A, k=B_, v=C, out=O, Bn=1, H=2, S=256, D=128, scale=0.1, mask=
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(out=None), -1),
     (dict(Bn=0), -1), (dict(H=0), -1), (dict(S=0), -1), (dict(P=0), -1), (dict(S=-5), -1),
     (dict(scale=math.inf), -1), (dict(scale=math.nan), -1), (dict(scale=-math.inf), -1),
+    (dict(scale=2.0 ** 64 * 1.0000001), -1), (dict(scale=-(2.0 ** 65)), -1), (dict(scale=3e38), -1),
     (dict(S=255, P=2), -2), (dict(S=32760, P=16), -2),
     (dict(D=32), -3), (dict(D=96), -3), (dict(D=256), -3), (dict(D=0), -3),
     (dict(q=A + 8), -4), (dict(k=B_ + 2), -4), (dict(v=C + 4), -4), (dict(out=O + 8), -4),
@@ -145,6 +149,39 @@ def test_valid_arguments_without_device_report_no_device(lib):
     assert _plain(lib) == -7
     assert _copy(lib) == -7
     assert _s2s(lib) == -7
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
+def test_largest_scale_passes_validation(lib):
+    assert _relayout(lib, scale=2.0 ** 64) == -7
+    assert _relayout(lib, scale=-(2.0 ** 64)) == -7
+    assert _instr(lib) == -7
+
+
+def _instr(lib, q=A, k=B_, v=C, out=O, Bn=1, H=2, S=256, D=128, P=2, scale=0.1, mask=None,
+           boundary=0, stamps=0x60000, words=None, units=None):
+    if words is None:
+        words = 64 * Bn * H * ((S + 127) // 128 + 1)
+    return lib.attn_fwd_relayout_instrumented_async(q, k, v, out, Bn, H, S, D, P, scale, mask,
+                                                    boundary, stamps, words, units, None)
+
+
+def test_instrumented_stamp_words(lib):
+    assert lib.attn_instrumented_stamp_words(1, 5, 32760) == 64 * 5 * (256 + 1)
+    assert lib.attn_instrumented_stamp_words(2, 3, 1) == 64 * 6 * 2
+    assert lib.attn_instrumented_stamp_words(0, 3, 100) == 0
+    assert binding.attn_instrumented_stamp_words(1, 1, 256) == 64 * 3
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(S=0), -1), (dict(scale=math.nan), -1),
+    (dict(boundary=3), -1), (dict(boundary=-1), -1), (dict(stamps=None), -1),
+    (dict(S=255, P=2), -2), (dict(D=64), -3), (dict(scale=-0.1), -3), (dict(scale=0.0), -3),
+    (dict(stamps=0x60004), -4), (dict(q=A + 8), -4),
+    (dict(words=64 * 2 * 3 - 1), -5), (dict(S=(1 << 23), P=1), -5),
+])
+def test_instrumented_validation(lib, kw, code):
+    assert _instr(lib, **kw) == code
 
 
 def test_python_binding_raises(lib):
