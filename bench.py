@@ -294,7 +294,7 @@ def write_profile_report(workload: str, d: str):
     flop = wl.flop_count(w.B, w.H, w.S, w.D, keep)
     stem = os.path.join(ROOT, "profiles", profile_prefix(workload))
     short = (f"python bench.py --workload {workload} --steps 30 --warmup 10 --overhead-pairs 4 "
-             "--no-cpu-baseline --no-clock")
+             "--no-cpu-baseline --no-clock --also none")
     sq1 = ("SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
            "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_MISC")
     sq2 = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS "
@@ -314,12 +314,16 @@ def write_profile_report(workload: str, d: str):
 
     stats_f = glob.glob(os.path.join(d, f"trace_{workload}", "**", "*kernel_stats.csv"), recursive=True)[0]
     stats = {r["Name"]: r for r in csv.DictReader(open(stats_f))}
-    def flags(n):                  # template flags after StoreMode: NEG, SPLIT, MASKED, SLAB_IN
+    def flags(n):   # template arguments after StoreMode: NEG, SPLIT, MASKED, SLAB_IN, INSTR
         return [x.strip() for x in n.split("(fa::StoreMode)")[1].split(">")[0].split(",")[1:]]
 
-    fused = sorted(n for n in stats if "fa_fwd" in n and "(fa::StoreMode)0" in n
-                   and flags(n)[-1] == "false")
-    slab_in = sorted(n for n in stats if "fa_fwd" in n and flags(n)[-1] == "true")
+    def product(n):                # not a timestamped instance
+        f = flags(n)
+        return len(f) < 5 or f[4] == "0"
+
+    fused = sorted(n for n in stats if "fa_fwd" in n and "(fa::StoreMode)0" in n and product(n)
+                   and flags(n)[3] == "false")
+    slab_in = sorted(n for n in stats if "fa_fwd" in n and product(n) and flags(n)[3] == "true")
     avg_s = {n: float(stats[n]["AverageNs"]) * 1e-9 for n in fused}
     call_s = sum(avg_s.values())
     bj = json.loads(open(os.path.join(d, f"bench_{workload}.json")).read().strip().splitlines()[-1])
@@ -347,8 +351,9 @@ def write_profile_report(workload: str, d: str):
           f"python bench.py --summarize trace {d}/trace_{workload}",
           "```\n",
           f"Kernel source sha256/16: {hsh}. StoreMode 0 = slab (fused re-layout), 1 = plain "
-          "[B][H][S][D] (the overhead twin and the serial baseline's attention). The last two "
-          "template flags of fa_fwd_pp_kernel: split-key units, masked units (false, false: whole "
+          "[B][H][S][D] (the overhead twin and the serial baseline's attention). Template "
+          "arguments of fa_fwd_pp_kernel after StoreMode: negative scale, split-key units, masked "
+          "units, slab-layout inputs, timestamped instance (false, false for the middle two: whole "
           "256-query tiles; true, false: split-key half tiles of a short last round, a second launch "
           "on the same stream; true, true: masked 128-query tiles). `relayout_kernel<16>`: the "
           "serial baseline's standalone copy.\n",
@@ -440,7 +445,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long", choices=sorted(WORKLOAD_KEYS))
     ap.add_argument("--also", default="video",
-                    help="comma-separated workloads also timed (fused call only), or ''")
+                    help="comma-separated workloads also timed (fused call only), or none")
     ap.add_argument("--overhead-pairs", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -590,7 +595,7 @@ def main():
 
     # ---- other workloads, fused call only (inputs resident, same timing).
     also = {}
-    for name in [x for x in a.also.split(",") if x and x != a.workload]:
+    for name in [x for x in a.also.split(",") if x and x not in ("none", a.workload)]:
         ow = wl.WORKLOADS[name]
         oi = wl.make(name)
         oq, ok_, ov = (t.to(dev) for t in (oi.q, oi.k, oi.v))

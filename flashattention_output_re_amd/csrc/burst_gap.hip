@@ -7,9 +7,10 @@
 // sender-visible time the pages model: stores are accepted and drain while
 // the producer moves on.  The gap is a dependent FMA chain whose length the
 // caller sets.  Stores complete (vmcnt) only at the very end -- unless the
-// caller asks for the completion-coupled form, where every wave waits for
-// its burst's stores to complete (vmcnt(0)) before the barrier that takes the
-// issue time, so a burst is only over once it has drained.
+// caller asks for the completion-coupled form, where every wave makes its
+// burst's stores visible device-wide (a release fence at device scope: L2
+// write-back, then the wait for completion) before the barrier that takes
+// the issue time, so a burst is only over once it has drained.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,7 +57,9 @@ __global__ __launch_bounds__(kThreads) void burst_gap_kernel(u32x4* dst, uint64_
       for (int c = tid; c < p.chunks; c += kThreads)
         base[c] = u32x4{(uint32_t)i, (uint32_t)k, (uint32_t)c, kMagic};
     }
-    if (p.coupled) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores completed
+    // Coupled: a device-scope release -- write back the L2 and wait until
+    // this wave's stores are complete, visible beyond this XCD.
+    if (p.coupled) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     barrier_no_fence();   // every wave has issued (coupled: completed) its stores
     const uint64_t t1 = __builtin_amdgcn_s_memtime();
     for (int g = 0; g < p.gap_iters; ++g) {

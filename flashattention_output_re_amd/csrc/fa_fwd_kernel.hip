@@ -2,12 +2,14 @@
 //
 // Persistent workgroups own output tiles of one (batch, head) at a time: they
 // stream the K/V tiles of the whole sequence through LDS, run QK^T and PV on
-// the bf16 MFMA units with an fp32 online softmax, and in the epilogue store
-// the finished tile straight into the P destination slabs of the
-// head-to-sequence re-layout, then move on to the next output tile without
-// waiting for those stores ("Technical Summary: X-Stage in DiT Inference",
-// Key Contributions 3: the output-tile owner issues the stores and resumes
-// the next tile's Q-loop; no dedicated communication wavefront).
+// the bf16 MFMA units with an fp32 online softmax, and in the epilogue issue
+// the next tile's first loads, then store the finished tile straight into the
+// P destination slabs of the head-to-sequence re-layout, and start the next
+// tile's Q-loop while those stores drain: the wait before it covers only the
+// loads ("Technical Summary: X-Stage in DiT Inference", Key Contributions 3:
+// the output-tile owner issues the stores and resumes the next tile's Q-loop;
+// no dedicated communication wavefront).  The kernel's header comment below
+// ("Tile boundary") gives the counter argument.
 // StoreMode::Plain runs the same body but writes [B][H][S][D].
 //
 // One kernel, fa_fwd_pp_kernel: 8 waves, one workgroup per CU, softmax and
@@ -577,8 +579,9 @@ __device__ __forceinline__ uint32_t clock_lo() { return (uint32_t)__builtin_amdg
 // when those stores were complete (INSTR 2 only, else 0), then the unit, the
 // workgroup and the high 32 bits of the clock at the store issue.  2 is the
 // completion-coupled counterfactual the pages contrast with piggybacking:
-// the owner issues its stores, waits for them to complete (vmcnt(0)), and
-// only then issues the next unit's prologue.  3 keeps the order in which the
+// the owner issues its stores, waits until they are complete and visible
+// beyond its XCD (a device-scope release: L2 write-back, vmcnt(0)), and only
+// then issues the next unit's prologue.  3 keeps the order in which the
 // stores come first and the next unit's prologue second, with one wait for
 // both (so the next Q-loop waits for the stores as well, though their drain
 // overlaps the prologue's loads).
@@ -1068,7 +1071,9 @@ void fa_fwd_pp_kernel(FwdParams p) {
         const uint64_t t = __builtin_amdgcn_s_memtime();
         uint32_t t_complete = 0;
         if constexpr (COUPLED) {
-          wait_vm<0>();   // the stores have completed
+          // The stores are complete and visible beyond this XCD (device-scope
+          // release: L2 write-back, then the wait for completion).
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
           t_complete = clock_lo();
           next_prologue();
         }

@@ -154,7 +154,8 @@ def measure(workload: str, reps: int = 5, seed_inputs=None) -> dict:
             e1.record(stream)
             torch.cuda.synchronize()
             times[m].append(e0.elapsed_time(e1))
-    res = {"workload": workload, "shape": {"B": w.B, "H": w.H, "S": w.S, "D": w.D, "P": w.P},
+    res = {"workload": workload, "kernel_source_sha256_16": source_hash(),
+           "shape": {"B": w.B, "H": w.H, "S": w.S, "D": w.D, "P": w.P},
            "masked": mask is not None, "reps": reps,
            "call_ms_median": {m: float(np.median(t)) for m, t in times.items()},
            "modes": {}}
@@ -174,12 +175,83 @@ def measure(workload: str, reps: int = 5, seed_inputs=None) -> dict:
     return res
 
 
+def source_hash() -> str:
+    """sha256/16 of the fused kernel's sources (as bench.py reports it)."""
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for name in ("fa_fwd_kernel.hip", "fa_fwd_kernel.h"):
+        with open(os.path.join(base, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def summarize(docs: list, command: str) -> str:
+    """Markdown summary of measure() results for one or more workloads."""
+    L = ["# Tile boundary of the fused kernel: per-tile timestamps\n",
+         "Command (from the repository root, after `python -m flashattention_output_re_amd.build`):\n",
+         "```", command, "python -m flashattention_output_re_amd.tile_stamps --summarize <those files>",
+         "```\n",
+         f"Kernel source sha256/16: {docs[0].get('kernel_source_sha256_16', '?')}.  Timestamped "
+         "instances of `fa_fwd_pp_kernel` (last template argument 1-3; include/fa_instrument.h) "
+         "record the low 32 bits of `s_memtime` per unit and wave; spans below are differences "
+         "within one workgroup, in shader cycles, over every pair of consecutive units a "
+         "workgroup runs (p50 / p90 over units x 8 waves).  Boundary forms: **piggyback** (the "
+         "product kernel's: next unit's Q loads and first K/V stages, then the tile's stores, "
+         "wait for the loads only), **ordered** (the stores, then the next unit's loads, one wait "
+         "for both: the previous form of this kernel), **coupled** (the stores made visible "
+         "device-wide by a device-scope release -- L2 write-back, wait for completion -- before "
+         "the next unit's loads: the completion-coupled counterfactual).\n",
+         "* issue span: last stage done -> last store instruction issued;",
+         "* held: last store issued -> the wait before the next Q-loop returned (the time the "
+         "owner is kept from resuming);",
+         "* to start: last store issued -> past the barrier that starts the next Q-loop;",
+         "* drain (coupled only): last store issued -> the stores complete and visible "
+         "device-wide: the span of one tile's stores from acceptance to completion;",
+         "* Q-loop: a unit's stage loop.\n"]
+    for d in docs:
+        sh = d["shape"]
+        L.append(f"## {d['workload']} (B={sh['B']}, H={sh['H']}, S={sh['S']}, D={sh['D']}, "
+                 f"P={sh['P']}{', block mask' if d['masked'] else ''})\n")
+        cm = d["call_ms_median"]
+        L.append("Whole call, median of alternated HIP-event timings: " + ", ".join(
+            f"{m} {cm[m]:.4f} ms" for m in ("product", "piggyback", "ordered", "coupled")) +
+            f" (coupled {100 * (cm['coupled'] / cm['piggyback'] - 1):+.1f} % against piggyback).\n")
+        L.append("| form | launch | Q-loop | issue span | held | to start | drain |")
+        L.append("|---|---|---|---|---|---|---|")
+        for m in ("piggyback", "ordered", "coupled"):
+            md = d["modes"][m]
+            assert md["output_equals_product"]
+            for ln, lname in (("first_launch", "whole tiles" if not d["masked"] else "masked tiles"),
+                              ("second_launch", "split half tiles")):
+                if ln not in md:
+                    continue
+                x = md[ln]
+
+                def c(k):
+                    s = x.get(k, {"n": 0})
+                    return "-" if not s["n"] else f"{s['p50_cyc']:.0f} / {s['p90_cyc']:.0f}"
+                L.append(f"| {m} | {lname} | {c('q_loop')} | {c('issue_span')} | "
+                         f"{c('resume_wait')} | {c('start_gap')} | {c('drain')} |")
+        L.append("\nOutputs of all three forms equal the product kernel's bit for bit.\n")
+    return "\n".join(L) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="video")
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--out", default=None)
+    ap.add_argument("--summarize", nargs="+", default=None, metavar="FILE",
+                    help="print the markdown summary of result files written with --out")
     a = ap.parse_args()
+    if a.summarize:
+        docs = [json.load(open(f)) for f in a.summarize]
+        cmd = "\n".join(f"python -m flashattention_output_re_amd.tile_stamps --workload "
+                         f"{d['workload']} --reps {d['reps']} --out {f}"
+                         for d, f in zip(docs, a.summarize))
+        print(summarize(docs, cmd), end="")
+        return
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     binding.load_library()
     res = measure(a.workload, a.reps)

@@ -15,8 +15,11 @@
  * burst_gap_run_async: `producers` workgroups of 256 threads, one per CU
  * (each asks for 96 KiB of LDS so no two share a CU), run `bursts` rounds:
  *   issue bytes_per_producer bytes of 16-byte stores (no wait for completion;
- *   coupled = 1: every wave then waits until its stores have completed, the
- *   completion-coupled issuer the pages contrast with the X-Stage view),
+ *   coupled = 1: every wave then makes its stores visible device-wide -- a
+ *   release fence at device scope, which writes the L2 back and waits for
+ *   completion -- the completion-coupled issuer the pages contrast with the
+ *   X-Stage view, remote visibility being visibility beyond the issuing
+ *   XCD's L2 on one GPU),
  *   workgroup barrier, then `gap_iters` iterations of a dependent FMA chain
  *   (the compute gap), workgroup barrier.
  * Chunk c (16 bytes) of producer k in burst i lands at byte offset

@@ -19,7 +19,9 @@
  *                unit's Q loads and first K/V stages are issued, then this
  *                unit's stores, and only the loads are waited for;
  *                1: the completion-coupled boundary -- the stores are issued
- *                and waited for (vmcnt(0)), then the next unit's loads;
+ *                and made visible device-wide (a device-scope release fence:
+ *                L2 write-back, wait for completion), then the next unit's
+ *                loads are issued;
  *                2: the stores, then the next unit's loads, with one wait
  *                for both (the stores drain while the loads are in flight,
  *                but the next Q-loop starts only once they are complete).

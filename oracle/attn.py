@@ -80,20 +80,22 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
               row_block: int = 128) -> np.ndarray:
     """softmax(scale Q K^T) V for every (batch, head).
 
-    q, k, v: float64 [B][H][S][D] (the exact values of the bf16 inputs).
-    mask_words: optional uint64 [H][nT][ceil(nT/64)] tile keep-mask, shared by
-    every batch index.  rows: optional query indices; the result then has
-    shape [B][H][len(rows)][D] instead of [B][H][S][D].
+    q, k: float64 [B][H][S][D] (the exact values of the bf16 inputs); v:
+    float64 [B][H][S][Dv], the values averaged (Dv = D for attention itself;
+    any width, since each output column is the same weighted sum of its own
+    value column).  mask_words: optional uint64 [H][nT][ceil(nT/64)] tile
+    keep-mask, shared by every batch index.  rows: optional query indices;
+    the result then has shape [B][H][len(rows)][Dv] instead of [B][H][S][Dv].
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, S, D = q.shape
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [B][H][S][D] shape")
+    if k.shape != q.shape or v.ndim != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must share one [B][H][S][D] shape, v [B][H][S][Dv]")
     keep = None if mask_words is None else unpack_mask(mask_words, S)
     n_out = S if rows is None else len(rows)
-    out = np.zeros((B, H, n_out, D), dtype=np.float64)
+    out = np.zeros((B, H, n_out, v.shape[3]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             kh = None if keep is None else keep[h]

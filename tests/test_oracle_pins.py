@@ -333,3 +333,25 @@ def test_planted_relayout_mistakes_are_caught():
 def test_oracle_passes_every_pin():
     assert failing_pins(_attn, oracle.relayout_split) == []
     assert failing_pins(_attn, oracle.relayout_index) == []
+
+
+def test_values_wider_than_keys_match_torch_sdpa():
+    """Value rows of another width than the keys (used to get the output for
+    V and for |V| from one softmax): torch's fp64 attention, which also takes
+    Dv != D, agrees, dense and with a tile mask."""
+    r = _rng(12)
+    for (B, H, S, D, Dv, masked) in [(1, 2, 40, 8, 24, False), (2, 1, 260, 16, 32, True)]:
+        q, k = (r.standard_normal((B, H, S, D)) for _ in range(2))
+        v = r.standard_normal((B, H, S, Dv))
+        mask_words, tmask = None, None
+        if masked:
+            keep = wl.tile_mask_bool(H, S, 0.5, seed=S)
+            mask_words = wl.pack_mask(keep)
+            tile = np.arange(S) // 128
+            tmask = torch.from_numpy(keep[:, tile][:, :, tile])[None]
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            attn_mask=tmask, scale=0.3).numpy()
+        got = oracle.attention(q, k, v, 0.3, mask_words)
+        assert got.shape == (B, H, S, Dv)
+        np.testing.assert_allclose(got, want, atol=1e-12, rtol=1e-12)
