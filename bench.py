@@ -43,11 +43,18 @@ WORKLOAD_KEYS = {"video": "video-dit-share", "long": "long-video-share",
 
 
 # What one fused call launches on its stream (the roofline's "launch" is that
-# call: HIP events bracket it).  Dense: the kernel over whole 256-query tiles,
-# plus, when the last round would fill at most half of the CUs, a second
-# launch of its split-key form for that round.  Masked: one launch of the
-# split-key form over 128-query tiles (one mask row each).
-def kernel_label(D: int, dense: bool) -> str:
+# call: HIP events bracket it).  Dense, with a workspace: the kernel over
+# whole 256-query tiles, whose last, partial round is spread over every CU as
+# equal slices of stages, then the merge launch of that round's partial
+# results.  Dense without a workspace: the kernel over whole tiles plus, when
+# the last round would fill at most half of the CUs, a second launch of its
+# split-key form for that round.  Masked: one launch of the split-key form
+# over 128-query tiles (one mask row each).
+def kernel_label(D: int, dense: bool, tail_spread: bool = False) -> str:
+    if dense and tail_spread:
+        return (f"fa_fwd_pp_kernel<{D}, Slab> (whole 256-query tiles, the last round's tiles "
+                "spread over every CU as stage slices) + fa_merge_kernel (the last round's "
+                "partial results)")
     if dense:
         return (f"fa_fwd_pp_kernel<{D}, Slab> (whole 256-query tiles; split-key half tiles "
                 "for a short last round)")
@@ -321,9 +328,11 @@ def write_profile_report(workload: str, d: str):
         f = flags(n)
         return len(f) < 5 or f[4] == "0"
 
-    fused = sorted(n for n in stats if "fa_fwd" in n and "(fa::StoreMode)0" in n and product(n)
-                   and flags(n)[3] == "false")
-    slab_in = sorted(n for n in stats if "fa_fwd" in n and product(n) and flags(n)[3] == "true")
+    fwd = [n for n in stats if "fa_fwd" in n]
+    fused = sorted([n for n in fwd if "(fa::StoreMode)0" in n and product(n)
+                    and flags(n)[3] == "false"] +
+                   [n for n in stats if "fa_merge" in n and "(fa::StoreMode)0" in n])
+    slab_in = sorted(n for n in fwd if product(n) and flags(n)[3] == "true")
     avg_s = {n: float(stats[n]["AverageNs"]) * 1e-9 for n in fused}
     call_s = sum(avg_s.values())
     bj = json.loads(open(os.path.join(d, f"bench_{workload}.json")).read().strip().splitlines()[-1])
@@ -355,8 +364,9 @@ def write_profile_report(workload: str, d: str):
           "arguments of fa_fwd_pp_kernel after StoreMode: negative scale, split-key units, masked "
           "units, slab-layout inputs, timestamped instance (false, false for the middle two: whole "
           "256-query tiles; true, false: split-key half tiles of a short last round, a second launch "
-          "on the same stream; true, true: masked 128-query tiles). `relayout_kernel<16>`: the "
-          "serial baseline's standalone copy.\n",
+          "on the same stream; true, true: masked 128-query tiles). `fa_merge_kernel`: the merge "
+          "of a dense call's last round, spread over every CU as stage slices (the workspace "
+          "entry points). `relayout_kernel<16>`: the serial baseline's standalone copy.\n",
           summary("trace", f"trace_{workload}"),
           f"One fused call = {' + '.join(f'{avg_s[n] * 1e3:.4f}' for n in fused)} = {call_s * 1e3:.4f} ms "
           f"under the tracer; {flop:.4g} algorithmic FLOP per call -> {flop / call_s / 1e12:.1f} TFLOP/s "
@@ -379,9 +389,9 @@ def write_profile_report(workload: str, d: str):
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cm.append(f"rocprofv3 --pmc {c} --output-format csv -d {d}/pmc_{c}_{workload} -o run -- "
                   f"{short} --copy-calibration-mib 1024")
-    cm.append(f"rocprofv3 --pmc {sq1} --kernel-include-regex fa_fwd --output-format csv "
+    cm.append(f"rocprofv3 --pmc {sq1} --kernel-include-regex fa_ --output-format csv "
               f"-d {d}/pmc_sq1_{workload} -o run -- {short}")
-    cm.append(f"rocprofv3 --pmc {sq2} --kernel-include-regex fa_fwd --output-format csv "
+    cm.append(f"rocprofv3 --pmc {sq2} --kernel-include-regex fa_ --output-format csv "
               f"-d {d}/pmc_sq2_{workload} -o run -- {short}")
     cm.append(f"python bench.py --summarize counters <dir>   # for each directory above")
     cm.append(f"python bench.py --summarize report:{workload} {d}   # this file")
@@ -444,6 +454,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long", choices=sorted(WORKLOAD_KEYS))
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="time the entry points without a workspace (last round as split "
+                         "half tiles) instead of the _ws_ ones")
     ap.add_argument("--also", default="video",
                     help="comma-separated workloads also timed (fused call only), or none")
     ap.add_argument("--overhead-pairs", type=int, default=30)
@@ -491,12 +504,26 @@ def main():
     slabs = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device=dev)
     plain = torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
+    # The workspace entry points (the dense tail round spread over every CU,
+    # its partial results merged by a second launch), workspace allocated
+    # here, outside the timed region.
+    ws_bytes = 0 if a.no_workspace else fa.attn_fwd_workspace_bytes(w.B, w.H, w.S, w.D)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def fused():
-        fa.attn_fwd_relayout_async(q, k, v, slabs, w.B, w.H, w.S, w.D, w.P, w.scale, mask, stream)
+        if a.no_workspace:
+            fa.attn_fwd_relayout_async(q, k, v, slabs, w.B, w.H, w.S, w.D, w.P, w.scale, mask,
+                                       stream)
+        else:
+            fa.attn_fwd_relayout_ws_async(q, k, v, slabs, w.B, w.H, w.S, w.D, w.P, w.scale, mask,
+                                          ws, stream)
 
     def plain_out():
-        fa.attn_fwd_plain_async(q, k, v, plain, w.B, w.H, w.S, w.D, w.scale, mask, stream)
+        if a.no_workspace:
+            fa.attn_fwd_plain_async(q, k, v, plain, w.B, w.H, w.S, w.D, w.scale, mask, stream)
+        else:
+            fa.attn_fwd_plain_ws_async(q, k, v, plain, w.B, w.H, w.S, w.D, w.scale, mask, ws,
+                                       stream)
 
     for _ in range(a.warmup):
         fused()
@@ -606,10 +633,12 @@ def main():
         oflop = wl.flop_count(ow.B, ow.H, ow.S, ow.D, okeep)
         oslabs = torch.empty((ow.P, ow.B, ow.S // ow.P, ow.H, ow.D), dtype=torch.bfloat16,
                              device=dev)
+        ows_bytes = 0 if a.no_workspace else fa.attn_fwd_workspace_bytes(ow.B, ow.H, ow.S, ow.D)
+        ows = torch.empty(max(ows_bytes, 16), dtype=torch.uint8, device=dev)
 
         def ofused():
-            fa.attn_fwd_relayout_async(oq, ok_, ov, oslabs, ow.B, ow.H, ow.S, ow.D, ow.P, ow.scale,
-                                       om, stream)
+            fa.attn_fwd_relayout_ws_async(oq, ok_, ov, oslabs, ow.B, ow.H, ow.S, ow.D, ow.P,
+                                          ow.scale, om, ows, stream)
 
         for _ in range(3):
             ofused()
@@ -650,7 +679,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": kernel_label(w.D, mask is None),
+                     "kernel": kernel_label(w.D, mask is None, ws_bytes > 0),
                      "mean_launch_ms": round(mean_launch_ms, 4),
                      "launch_ms_p10_p50_p90": [round(float(np.percentile(launch_ms, x)), 4)
                                                for x in (10, 50, 90)]},
@@ -666,6 +695,7 @@ def main():
             "speedup_fused_over_serial": round(serial_ms / mean_launch_ms, 4),
         },
         "also": also,
+        "workspace_bytes": ws_bytes,
         "slab_to_slab": {
             "what": "attn_fwd_slab_to_slab: q, k, v read from [P][B][S/P][H][D] slabs (the "
                     "pre-attention exchange fused into the loads) and the output stored into slabs",

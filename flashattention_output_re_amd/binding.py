@@ -43,13 +43,18 @@ SIGNATURES = {
     "attn_fwd_relayout_instrumented_async": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _P,
                                              ctypes.c_int64, _P, _P],
     "attn_instrumented_stamp_words": [_I, _I, _I],
+    "attn_fwd_relayout_ws_async": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P,
+                                   ctypes.c_int64, _P],
+    "attn_fwd_plain_ws_async": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, ctypes.c_int64, _P],
+    "attn_fwd_workspace_bytes": [_I, _I, _I, _I],
     "attn_status_string": [_I],
     "attn_abi_version": [],
 }
 
 
 RESTYPES = {"attn_status_string": ctypes.c_char_p,
-            "attn_instrumented_stamp_words": ctypes.c_int64}
+            "attn_instrumented_stamp_words": ctypes.c_int64,
+            "attn_fwd_workspace_bytes": ctypes.c_int64}
 
 
 class FaError(RuntimeError):
@@ -217,6 +222,59 @@ def relayout_to_slabs(plain, out_slabs, B, H, S, D, P):
     _check_relayout(plain, out_slabs, B, H, S, D, P)
     st = load_library().relayout_to_slabs(_ptr(plain), _ptr(out_slabs), B, H, S, D, P)
     _raise(st, "relayout_to_slabs")
+
+
+def attn_fwd_workspace_bytes(B: int, H: int, S: int, D: int) -> int:
+    """Workspace bytes a dense _ws_ call needs on the current device."""
+    n = int(load_library().attn_fwd_workspace_bytes(B, H, S, D))
+    _raise(n if n < 0 else FA_OK, "attn_fwd_workspace_bytes")
+    return n
+
+
+def _workspace(workspace, B, H, S, D, device):
+    """The caller's workspace tensor, or one from torch's allocator."""
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        return workspace
+    n = attn_fwd_workspace_bytes(B, H, S, D)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def attn_fwd_relayout_ws_async(q, k, v, out_slabs, B, H, S, D, P, scale, mask=None,
+                               workspace=None, stream=None):
+    """Fused attention + slab store with the tail round spread over every
+    workgroup; workspace: a device tensor of at least
+    attn_fwd_workspace_bytes(B, H, S, D) bytes (allocated here when None)."""
+    if P > 0 and S % P == 0:
+        for n, t in (("q", q), ("k", k), ("v", v)):
+            _check_tensor(n, t, (B, H, S, D))
+        _check_tensor("out_slabs", out_slabs, (P, B, S // P, H, D))
+        _check_mask(mask, H, S)
+    ws = _workspace(workspace, B, H, S, D, q.device)
+    st = load_library().attn_fwd_relayout_ws_async(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out_slabs), B, H, S, D, P, float(scale), _ptr(mask),
+        _ptr(ws), _nbytes(ws), _stream(stream))
+    _raise(st, "attn_fwd_relayout_ws_async")
+    return ws
+
+
+def attn_fwd_plain_ws_async(q, k, v, out, B, H, S, D, scale, mask=None, workspace=None,
+                            stream=None):
+    """The plain-layout twin of attn_fwd_relayout_ws_async."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_tensor(n, t, (B, H, S, D))
+    _check_mask(mask, H, S)
+    ws = _workspace(workspace, B, H, S, D, q.device)
+    st = load_library().attn_fwd_plain_ws_async(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, float(scale), _ptr(mask), _ptr(ws),
+        _nbytes(ws), _stream(stream))
+    _raise(st, "attn_fwd_plain_ws_async")
+    return ws
 
 
 def attn_instrumented_stamp_words(B: int, H: int, S: int) -> int:

@@ -97,15 +97,31 @@ void div_magic(uint32_t d, uint32_t* magic, int* shift) {
 }
 
 // How one dense call splits into launches: `whole` units of whole 256-query
-// tiles on up to `cap` workgroups, then (split_units > 0) the last round's
-// tiles as 2 x tail half tiles in a second launch on up to `split_cap`.
+// tiles on up to `cap` workgroups, then either (split_units > 0) the last
+// round's tiles as 2 x tail half tiles in a second launch on up to
+// `split_cap`, or (tail > 0, with a workspace) the last round's `tail` tiles
+// as one span of tail * ns stages that the `cap` workgroups of the first
+// launch share in slices of tail_len stages, their partial results merged by
+// a second, small launch.
 struct DensePlan {
   int whole_units = 0, split_units = 0, cap = 0, split_cap = 0;
+  int tail = 0, tail_len = 0;
+  int64_t ws_bytes = 0;    // workspace the tail round needs
 };
+
+// The shortest slice (in 64-key stages) for which the tail round is spread
+// over the workgroups: each slice writes a ~136 KiB partial that the merge
+// reads back, which a slice of 64 stages (~0.1 ms) hides and a slice of a
+// dozen does not (the Image share's 12-stage slices measured 7% slower than
+// the split half tiles); shorter slices keep the schedule without a
+// workspace.
+constexpr int kTailMinSlice = 64;
 
 // Launch geometry of a call with params p (units = every tile): the number
 // of units per launch and the persistent grid caps, or FA_EDEVICE.
-int plan_call(int D, fa::StoreMode mode, bool masked, const fa::FwdParams& p, DensePlan* plan) {
+// use_ws: the caller brings a workspace, so the tail round may be spread.
+int plan_call(int D, fa::StoreMode mode, bool masked, const fa::FwdParams& p, DensePlan* plan,
+              bool use_ws = false) {
   const fa::Variant var = masked ? fa::Variant::Masked : fa::Variant::Whole;
   const int cap = grid_cap_for(D, mode, var);
   if (cap <= 0) return FA_EDEVICE;
@@ -119,6 +135,18 @@ int plan_call(int D, fa::StoreMode mode, bool masked, const fa::FwdParams& p, De
   // time of a whole tile), in a second launch on the same stream.
   const int tail = p.units % cap;
   const int stages = (p.S + 63) / 64;
+  const int64_t span = (int64_t)tail * stages;
+  const int64_t slice = (span + cap - 1) / cap;
+  if (use_ws && tail > 0 && slice >= kTailMinSlice) {
+    // Every slot takes tail_len <= stages stages of the span, so a slice
+    // meets at most two tiles: two workspace slots per slot that has one.
+    plan->whole_units = p.units - tail;
+    plan->tail = tail;
+    plan->tail_len = (int)slice;
+    const int64_t slices = (span + slice - 1) / slice;
+    plan->ws_bytes = 2 * slices * (int64_t)fa::seg_floats(D) * 4;
+    return FA_OK;
+  }
   if (tail == 0 || 2 * tail > cap || stages < 2) return FA_OK;
   const int split_cap = grid_cap_for(D, mode, fa::Variant::Split);
   if (split_cap <= 0) return FA_EDEVICE;
@@ -172,6 +200,15 @@ int launch_call(int D, fa::StoreMode mode, const fa::FwdParams& p, const DensePl
                 hipStream_t stream, bool slab_in, int instr) {
   const bool masked = p.mask != nullptr;
   const fa::Variant var = masked ? fa::Variant::Masked : fa::Variant::Whole;
+  if (plan.tail > 0) {
+    if (!p.ws || instr) return FA_ELAUNCH;
+    fa::FwdParams whole = p;
+    whole.units = plan.whole_units;
+    whole.tail = plan.tail;
+    whole.tail_len = plan.tail_len;
+    if (fa::launch_fwd(D, mode, var, whole, plan.cap, stream, slab_in, 0) != 0) return FA_ELAUNCH;
+    return fa::launch_merge(D, mode, whole, stream) == 0 ? FA_OK : FA_ELAUNCH;
+  }
   if (plan.whole_units > 0) {
     fa::FwdParams whole = p;
     whole.units = plan.whole_units;
@@ -200,6 +237,34 @@ int run(fa::StoreMode mode, const void* q, const void* k, const void* v, void* o
   st = plan_call(D, mode, mask != nullptr, p, &plan);
   if (st != FA_OK) return st;
   return launch_call(D, mode, p, plan, stream, slab_in, 0);
+}
+
+// A workspace argument: null only when the call needs none (ws_bytes == 0 is
+// then allowed too), else 16-byte aligned and at least `need` bytes.
+int check_workspace(const void* ws, int64_t ws_bytes, int64_t need) {
+  if (need == 0) return FA_OK;
+  if (!ws) return FA_EINVAL;
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return FA_EALIGN;
+  if (ws_bytes < need) return FA_ERANGE;
+  return FA_OK;
+}
+
+// Dense calls with a workspace: the tail round spread over every workgroup.
+// Masked calls need no workspace and run as without one.
+int run_ws(fa::StoreMode mode, const void* q, const void* k, const void* v, void* out, int B,
+           int H, int S, int D, int P, float scale, const uint64_t* mask, void* ws,
+           int64_t ws_bytes, hipStream_t stream) {
+  fa::FwdParams p;
+  int st = make_params(mode, q, k, v, out, B, H, S, D, P, scale, mask, false, &p);
+  if (st != FA_OK) return st;
+  if (ws_bytes < 0) return FA_EINVAL;
+  DensePlan plan;
+  st = plan_call(D, mode, mask != nullptr, p, &plan, true);
+  if (st != FA_OK) return st;
+  st = check_workspace(ws, ws_bytes, plan.ws_bytes);
+  if (st != FA_OK) return st;
+  p.ws = static_cast<float*>(ws);
+  return launch_call(D, mode, p, plan, stream, false, 0);
 }
 
 int validate_relayout(const void* plain, const void* out, int B, int H, int S, int D, int P) {
@@ -291,6 +356,36 @@ int relayout_to_slabs_async(const void* plain, void* out_slabs, int B, int H, in
 
 int relayout_to_slabs(const void* plain, void* out_slabs, int B, int H, int S, int D, int P) {
   return finish_blocking(run_relayout(plain, out_slabs, B, H, S, D, P, nullptr));
+}
+
+int attn_fwd_relayout_ws_async(const void* q, const void* k, const void* v, void* out_slabs,
+                               int B, int H, int S, int D, int P, float scale,
+                               const uint64_t* mask, void* workspace, int64_t workspace_bytes,
+                               void* stream) {
+  return run_ws(fa::StoreMode::Slab, q, k, v, out_slabs, B, H, S, D, P, scale, mask, workspace,
+                workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_plain_ws_async(const void* q, const void* k, const void* v, void* out, int B, int H,
+                            int S, int D, float scale, const uint64_t* mask, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+  return run_ws(fa::StoreMode::Plain, q, k, v, out, B, H, S, D, 1, scale, mask, workspace,
+                workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int64_t attn_fwd_workspace_bytes(int B, int H, int S, int D) {
+  if (B <= 0 || H <= 0 || S <= 0) return FA_EINVAL;
+  if (D != 64 && D != 128) return FA_EUNSUPPORTED;
+  if (((int64_t)S + 256) * D * 2 > (int64_t)INT32_MAX) return FA_ERANGE;
+  const int64_t tiles = (int64_t)B * H * ((S + 255) / 256);
+  if (tiles > (int64_t)INT32_MAX) return FA_ERANGE;
+  fa::FwdParams p{};
+  p.S = S;
+  p.units = (int)tiles;
+  DensePlan plan;
+  const int st = plan_call(D, fa::StoreMode::Slab, false, p, &plan, true);
+  if (st != FA_OK) return st;
+  return plan.ws_bytes;
 }
 
 int attn_fwd_relayout_instrumented_async(const void* q, const void* k, const void* v,

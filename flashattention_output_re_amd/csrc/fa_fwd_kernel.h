@@ -38,7 +38,22 @@ struct FwdParams {
   // Instrumented launches only: per-unit timestamp records (8 uint32 per
   // unit and wave), else nullptr.
   uint32_t* stamps;
+  // Whole form only: the tail round, run after the launch's `units` whole
+  // units as one span of tail * ns stages (ns = ceil(S / 64)) of the next
+  // `tail` tiles, workgroup slot sid taking [sid * tail_len, (sid + 1) *
+  // tail_len); partial results go to ws (seg_floats(D) floats per slot, two
+  // slots per workgroup) and fa_merge_kernel stores those tiles.  tail = 0:
+  // no tail round.
+  int tail, tail_len;
+  float* ws;
 };
+
+// Workspace slot of one tail segment, in floats: per wave (8) and lane (64)
+// the O^T accumulator divided by the row sum, as D / 8 quads of floats
+// ([wave][quad][lane][4]), then per wave and lane {running max, row sum, 0,
+// 0} from seg_ml_offset(D) on.
+constexpr int seg_ml_offset(int D) { return 8 * (D / 8) * 64 * 4; }
+constexpr int seg_floats(int D) { return seg_ml_offset(D) + 8 * 64 * 4; }
 
 // Launch with at most `grid_cap` persistent workgroups; 0 on success.
 // slab_in: q, k, v are [P][B][S/P][H][D] (sequence-sharded) instead of
@@ -49,6 +64,9 @@ struct FwdParams {
 // one wait for both.
 int launch_fwd(int D, StoreMode mode, Variant var, const FwdParams& p, int grid_cap,
                hipStream_t stream, bool slab_in = false, int instr = 0);
+// The merge kernel of a call's tail round (p.tail tiles, p.ws), on the
+// stream after the whole-form launch that wrote the partials; 0 on success.
+int launch_merge(int D, StoreMode mode, const FwdParams& p, hipStream_t stream);
 // Resident workgroups per CU for the instance (D, mode, var); 0 on success.
 int kernel_occupancy(int D, StoreMode mode, Variant var, int* blocks_per_cu);
 

@@ -630,12 +630,6 @@ void fa_fwd_pp_kernel(FwdParams p) {
   const int ns = (p.S + BN - 1) / BN;                               // K/V stages (dense)
   const int nsh = (ns + 1) / 2;                                     // stages per stream (SPLIT)
   const int own = SPLIT ? grp : 0;   // the stream this wave computes on and (SPLIT) loads
-  // Stage j of this wave's stream starts at key key_of(j); a stage past the
-  // end is read at key S, which the buffer returns as zeros.
-  auto key_of = [&](int j) FA_INL {
-    const int st = own * nsh + j;
-    return st < ns ? st * BN : p.S;
-  };
   // Stage j of the stream sits in kbuf(j % NBUF) / vbuf(j % NBUF).
   auto kbuf = [&](int slot) FA_INL -> uint16_t* {
     if (NBUF == 4 && slot == 2) return kb2[own];
@@ -677,17 +671,21 @@ void fa_fwd_pp_kernel(FwdParams p) {
   }
 
   // A work unit: dense, 256-query tile `tile` (split units: its half
-  // unit & 1); masked, 128-query tile qt of head bh, which is mask row qt.
+  // unit & 1); masked, 128-query tile qt of head bh, which is mask row qt;
+  // a segment (whole form, tail round): stages [s0, s0 + nst) of a
+  // 256-query tile, whose partial result goes to workspace slot seg.
   // [B][H][S][D] inputs: one buffer resource per head slice.  Slab inputs:
   // one per tensor, with the head's columns at head_col of every row.
+  // Stage j of this wave's stream starts at key s0 + j (j < nst, in stages);
+  // nloop stages are run (split units: as many for both groups, the stages
+  // past the stream's end reading zeros).
   struct Unit {
-    int bh, qt, b, h, qrow;
+    int uidx, bh, qt, b, h, qrow;
+    int s0, nst, nloop, seg;
     uint32_t head_col;
     __amdgpu_buffer_rsrc_t rq, rk, rv;
   };
-  auto make_unit = [&](int unit) FA_INL {
-    Unit u;
-    const int tile = MASKED ? unit : SPLIT ? p.unit_base + (unit >> 1) : unit;
+  auto make_tile = [&](int tile, Unit& u) FA_INL {
     u.bh = tile / p.nqt;
     u.qt = tile - u.bh * p.nqt;
     u.b = u.bh / p.H;
@@ -698,11 +696,51 @@ void fa_fwd_pp_kernel(FwdParams p) {
     u.rk = make_rsrc(p.k + head_off, in_size);
     u.rv = make_rsrc(p.v + head_off, in_size);
     u.head_col = (uint32_t)u.h * D * 2;
+  };
+  auto make_unit = [&](int unit) FA_INL {
+    Unit u;
+    make_tile(MASKED ? unit : SPLIT ? p.unit_base + (unit >> 1) : unit, u);
+    u.uidx = unit;
     u.qrow = MASKED  ? u.qt * BM + wq * 32 + l32
              : SPLIT ? u.qt * 256 + (unit & 1) * 128 + wq * 32 + l32
                      : u.qt * 256 + wave * 32 + l32;
+    u.s0 = own * nsh;
+    u.nst = SPLIT ? (ns - u.s0 < nsh ? ns - u.s0 : nsh) : ns;
+    u.nloop = SPLIT ? nsh : ns;
+    u.seg = -1;
     return u;
   };
+  // Tail segments (whole form): the tail round's t tiles, after the launch's
+  // whole units, are one span of t * ns stages, of which the workgroup in
+  // slot sid runs [sid * L, (sid + 1) * L), L = p.tail_len <= ns: at most two
+  // segments, the end of one tile and the start of the next.  Segment j of
+  // slot sid writes workspace slot 2 sid + j.
+  auto tail_segments = [&](int sid) FA_INL {
+    if (SPLIT || MASKED || p.tail <= 0) return 0;
+    const int a = sid * p.tail_len;
+    const int b = a + p.tail_len < p.tail * ns ? a + p.tail_len : p.tail * ns;
+    if (a >= b) return 0;
+    return (b - 1) / ns > a / ns ? 2 : 1;
+  };
+  auto make_segment = [&](int sid, int j) FA_INL {
+    Unit u;
+    const int a = sid * p.tail_len;
+    const int b = a + p.tail_len < p.tail * ns ? a + p.tail_len : p.tail * ns;
+    const int ti = a / ns + j;
+    const int st0 = j == 0 ? a - ti * ns : 0;
+    const int st1 = (b < (ti + 1) * ns ? b : (ti + 1) * ns) - ti * ns;
+    make_tile(p.units + ti, u);
+    u.uidx = -1;
+    u.qrow = u.qt * 256 + wave * 32 + l32;
+    u.s0 = st0;
+    u.nst = st1 - st0;
+    u.nloop = st1 - st0;
+    u.seg = 2 * sid + j;
+    return u;
+  };
+  // First key of stage j of unit u's stream; a stage past the end is read
+  // at key S, which the buffer returns as zeros.
+  auto key_of = [&](const Unit& u, int j) FA_INL { return j < u.nst ? (u.s0 + j) * BN : p.S; };
   // Slab inputs: byte offset of the row of token s < S of unit u's (b, h).
   auto slab_row = [&](const Unit& u, uint32_t s) FA_INL {
     const uint32_t ps = (__umulhi(s, p.sp_magic) + s) >> p.sp_shift;
@@ -745,20 +783,19 @@ void fa_fwd_pp_kernel(FwdParams p) {
   };
   // Masked units: this group's stream of kept stages, and the first keys of
   // stages n, n + 1 and n + 2 of the stream (key_n[0..2]), advanced after
-  // each stage.  nloop: the stages of this wave's stream in the unit.
+  // each stage; the unit's nloop is the stream's number of stages.
   KeptStages kept;
   int key_n[3] = {0, 0, 0};
-  int nloop = SPLIT ? nsh : ns;
-  auto start_stream = [&](const Unit& u) FA_INL {
+  auto start_stream = [&](Unit& u) FA_INL {
     if constexpr (MASKED) {
-      nloop = kept.init(p.mask + ((size_t)u.h * p.nmt + u.qt) * p.mw, p.nmt, p.mw, p.S, own);
+      u.nloop = kept.init(p.mask + ((size_t)u.h * p.nmt + u.qt) * p.mw, p.nmt, p.mw, p.S, own);
       key_n[0] = kept.next();
       key_n[1] = kept.next();
       key_n[2] = kept.next();
     }
   };
   // First key of stage j of this wave's stream.
-  auto stage_key = [&](int j) FA_INL { return MASKED ? key_n[j] : key_of(j); };
+  auto stage_key = [&](const Unit& u, int j) FA_INL { return MASKED ? key_n[j] : key_of(u, j); };
   // This wave's share of unit u's K or V stage that starts at key `key`
   // into slot `slot`.
   auto dma_k = [&](const Unit& u, int slot, int key) FA_INL {
@@ -793,16 +830,16 @@ void fa_fwd_pp_kernel(FwdParams p) {
     for (int ks = 0; ks < NKS; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, load16(u.rq, qbase + ks * 32 + g * 16));
     if (SPLIT || grp == 0) {
-      dma_k(u, 0, stage_key(0));
-      dma_k(u, 1, stage_key(1));
+      dma_k(u, 0, stage_key(u, 0));
+      dma_k(u, 1, stage_key(u, 1));
     }
-    if (!SPLIT && grp == 0) dma_k(u, 2, key_of(2));
+    if (!SPLIT && grp == 0) dma_k(u, 2, key_of(u, 2));
     if (SPLIT) {
-      dma_v(u, 0, stage_key(0));
+      dma_v(u, 0, stage_key(u, 0));
     } else if (grp == 1) {
-      dma_v(u, 0, stage_key(0));
-      dma_v(u, 1, stage_key(1));
-      dma_v(u, 2, key_of(2));
+      dma_v(u, 0, stage_key(u, 0));
+      dma_v(u, 1, stage_key(u, 1));
+      dma_v(u, 2, key_of(u, 2));
     }
   };
 
@@ -819,18 +856,18 @@ void fa_fwd_pp_kernel(FwdParams p) {
   auto stage_dma = [&](auto SLOT, int n) FA_INL {
     constexpr int slot = decltype(SLOT)::value;
     if (SPLIT) {
-      dma_k(cur, slot, MASKED ? key_n[2] : key_of(n + 2));
-      dma_v(cur, (slot + 1) % NBUF, MASKED ? key_n[1] : key_of(n + 1));
+      dma_k(cur, slot, MASKED ? key_n[2] : key_of(cur, n + 2));
+      dma_v(cur, (slot + 1) % NBUF, MASKED ? key_n[1] : key_of(cur, n + 1));
     } else if constexpr (!SLAB_IN) {
       // One code path for both groups (the tensor and slot selected, not
       // branched on): the softmax wave takes no branch to issue its DMA.
       constexpr int sl = (slot + 3) % NBUF;
       uint16_t* const dst = (grp == 0 ? kbuf(sl) : vbuf(sl)) + 64 * 8 * PW * wq;
-      dma_blocks<PW>(dst, grp == 0 ? cur.rk : cur.rv, (uint32_t)key_of(n + 3) * (D * 2), koff);
+      dma_blocks<PW>(dst, grp == 0 ? cur.rk : cur.rv, (uint32_t)key_of(cur, n + 3) * (D * 2), koff);
     } else if (grp == 0) {
-      dma_k(cur, (slot + 3) % NBUF, key_of(n + 3));
+      dma_k(cur, (slot + 3) % NBUF, key_of(cur, n + 3));
     } else {
-      dma_v(cur, (slot + 3) % NBUF, key_of(n + 3));
+      dma_v(cur, (slot + 3) % NBUF, key_of(cur, n + 3));
     }
   };
   // Split units, [B][H][S][D] inputs: the same stages as DmaPlans, issued
@@ -839,9 +876,10 @@ void fa_fwd_pp_kernel(FwdParams p) {
   auto split_plans = [&](auto SLOT, int n) FA_INL {
     constexpr int slot = decltype(SLOT)::value;
     const int wofs = 64 * 8 * PW * wq;
-    return SplitPlans{plan_of(kbuf(slot) + wofs, cur.rk, koff, MASKED ? key_n[2] : key_of(n + 2)),
+    return SplitPlans{plan_of(kbuf(slot) + wofs, cur.rk, koff,
+                              MASKED ? key_n[2] : key_of(cur, n + 2)),
                       plan_of(vbuf((slot + 1) % NBUF) + wofs, cur.rv, voff,
-                              MASKED ? key_n[1] : key_of(n + 1))};
+                              MASKED ? key_n[1] : key_of(cur, n + 1))};
   };
 
   // Region S(n), SLOT = n % NBUF: this wave's DMA, the softmax of stage n,
@@ -851,7 +889,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
   // prologue, which the tile boundary waited for): S(0) and S(1) of a whole
   // unit, S(0) of a split unit.
   auto region_s = [&](auto SLOT, int n, StageProbs<NEG>& sm) FA_INL {
-    const int key0 = MASKED ? key_n[0] : (own * nsh + n) * BN;
+    const int key0 = MASKED ? key_n[0] : key_of(cur, n);
     if constexpr (SPLIT && !SLAB_IN) {
       const SplitPlans pl = split_plans(SLOT, n);
       mask_tail(s, key0, p.S, g, fill);
@@ -956,6 +994,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
   };
   // A unit's stages.
   auto stages = [&]() FA_INL {
+    const int nloop = cur.nloop;
     for (int n = 0; n < nloop; n += NBUF) {
       stage(std::integral_constant<int, 0>{}, n);
       if (n + 1 >= nloop) break;
@@ -969,13 +1008,21 @@ void fa_fwd_pp_kernel(FwdParams p) {
     }
   };
 
-  // Dense units in XCD-aware order.  Masked units keep the plain order: on a
-  // 30%-dense block mask the XCD-aware order measured slower (its workgroups
-  // skip different tiles, so they do not stream K/V in step as dense tiles
-  // do).
-  int unit = MASKED ? (int)blockIdx.x : xcd_slot(blockIdx.x, gridDim.x);
-  if (unit >= p.units) return;
-  cur = make_unit(unit);
+  // This workgroup's work items: the launch's units slot, slot + G, ... and
+  // then (whole form) its tail segments.  Dense units in XCD-aware order.
+  // Masked units keep the plain order: on a 30%-dense block mask the
+  // XCD-aware order measured slower (its workgroups skip different tiles, so
+  // they do not stream K/V in step as dense tiles do).
+  const int G = (int)gridDim.x;
+  const int slot = MASKED ? (int)blockIdx.x : xcd_slot(blockIdx.x, G);
+  const int n_units = slot < p.units ? (p.units - slot + G - 1) / G : 0;
+  const int n_items = n_units + tail_segments(slot);
+  auto make_item = [&](int i) FA_INL {
+    return i < n_units ? make_unit(slot + i * G) : make_segment(slot, i - n_units);
+  };
+  if (n_items == 0) return;
+  int item = 0;
+  cur = make_item(0);
   start_stream(cur);
   prologue(cur);
   wait_vm<0>();
@@ -1048,12 +1095,11 @@ void fa_fwd_pp_kernel(FwdParams p) {
 
     // The tile boundary: the next unit's prologue, then this unit's stores
     // (COUPLED: the stores, their completion, then the prologue).
-    const int next = unit + (int)gridDim.x;
-    const bool more = next < p.units;
+    const bool more = item + 1 < n_items;
     Unit nxt = cur;
     auto next_prologue = [&]() FA_INL {
       if (more) {
-        nxt = make_unit(next);
+        nxt = make_item(item + 1);
         start_stream(nxt);
         prologue(nxt);
       }
@@ -1079,9 +1125,10 @@ void fa_fwd_pp_kernel(FwdParams p) {
         }
         if constexpr (LATE) next_prologue();
         // Lanes 0 and 1 write the record; the others write the sink.
-        uint32_t* const rec = p.stamps + ((size_t)unit * 8 + wave) * 8;
+        // (Instrumented launches have no tail segments: cur.uidx >= 0.)
+        uint32_t* const rec = p.stamps + ((size_t)cur.uidx * 8 + wave) * 8;
         const u32x4 val = lane == 0 ? u32x4{t_ready, t_start, t_epi, (uint32_t)t}
-                                    : u32x4{t_complete, (uint32_t)unit, (uint32_t)blockIdx.x,
+                                    : u32x4{t_complete, (uint32_t)cur.uidx, (uint32_t)blockIdx.x,
                                             (uint32_t)(t >> 32)};
         u32x4* const to = lane < 2 ? reinterpret_cast<u32x4*>(rec) + lane
                                    : reinterpret_cast<u32x4*>(fa_store_sink) + lane;
@@ -1093,9 +1140,26 @@ void fa_fwd_pp_kernel(FwdParams p) {
         wait_vm<nst>();
     };
     // Whole units: every wave stores its 32 queries.  Split units: group 0
-    // stores the merged tile, group 1 nothing.
+    // stores the merged tile, group 1 nothing.  Tail segments: every wave
+    // writes its partial result -- the O^T accumulator normalised by its own
+    // row sum (the same products store_rows forms, so the accumulator is
+    // not kept twice), its running max and that row sum -- to workspace slot
+    // cur.seg for the merge kernel (layout: seg_floats).
     if (SPLIT && grp == 1) {
       finish(std::integral_constant<int, 0>{});
+    } else if (!SPLIT && !MASKED && cur.seg >= 0) {
+      float* const ws = p.ws + (size_t)cur.seg * seg_floats(D);
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          *reinterpret_cast<f32x4*>(ws + ((wave * 4 * NDB + db * 4 + rr) * 64 + lane) * 4) =
+              f32x4{acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv, acc[db][4 * rr + 2] * inv,
+                    acc[db][4 * rr + 3] * inv};
+      *reinterpret_cast<f32x4*>(ws + seg_ml_offset(D) + (wave * 64 + lane) * 4) =
+          f32x4{m_run, l_tot, 0.0f, 0.0f};
+      finish(std::integral_constant<int, 4 * NDB + 1>{});
     } else {
       store_rows<D, MODE, NDB>(p, acc, inv, cur.qrow, 0, cur.b, cur.h, cur.bh, g, lane);
       finish(std::integral_constant<int, 2 * NDB>{});
@@ -1103,8 +1167,63 @@ void fa_fwd_pp_kernel(FwdParams p) {
     if constexpr (INSTR) t_ready = clock_lo();
     if (!more) break;
     cur = nxt;
-    unit = next;
+    ++item;
   }
+}
+
+// Merge of a dense call's tail round: one workgroup of 8 waves per tail tile,
+// each lane standing where the fused kernel's lane with the same query and
+// dims stood.  The tile's partial results are the workspace slots of the
+// workgroups whose slice of the tail span [sid L, (sid + 1) L) overlaps its
+// stages [ti ns, (ti + 1) ns): slot 2 sid for the first tile of a slice,
+// 2 sid + 1 for the second.  Each partial holds its output normalised by its
+// own row sum l, taken against its own running max m (log2 domain); with m*
+// the largest m and weights w = 2^(m - m*) l, O = sum w O_part / sum w, the
+// partials taken in slice order, and the tile is rounded and stored like a
+// whole unit's.
+template <int D, StoreMode MODE>
+__global__ __launch_bounds__(512) void fa_merge_kernel(FwdParams p) {
+  constexpr int NDB = D / 32;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int ns = (p.S + BN - 1) / BN;
+  const int ti = blockIdx.x;
+  const int tile = p.units + ti;
+  const int bh = tile / p.nqt, qt = tile - bh * p.nqt;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int L = p.tail_len;
+  const int w0 = ti * ns / L, w1 = ((ti + 1) * ns - 1) / L;
+  auto part = [&](int sid) FA_INL {
+    return p.ws + (size_t)(2 * sid + (sid * L / ns == ti ? 0 : 1)) * seg_floats(D);
+  };
+  float m = -3.0e38f;
+  for (int sid = w0; sid <= w1; ++sid)
+    m = fmaxf(m, reinterpret_cast<const f32x4*>(part(sid) + seg_ml_offset(D))[wave * 64 + lane][0]);
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+  float l = 0.0f;
+  for (int sid = w0; sid <= w1; ++sid) {
+    const float* const ws = part(sid);
+    const f32x4 ml = reinterpret_cast<const f32x4*>(ws + seg_ml_offset(D))[wave * 64 + lane];
+    const float a = __builtin_amdgcn_exp2f(ml[0] - m) * ml[1];
+    l += a;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4 o =
+            reinterpret_cast<const f32x4*>(ws)[(wave * 4 * NDB + db * 4 + rr) * 64 + lane];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[db][4 * rr + k] = __builtin_fmaf(a, o[k], acc[db][4 * rr + k]);
+      }
+  }
+  // l is already the whole row's (each partial's sum covers both wave halves).
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  store_rows<D, MODE, NDB>(p, acc, inv, qt * 256 + wave * 32 + l32, 0, b, h, bh, g, lane);
 }
 
 // Kernel form of each variant: split-key units, masked units.
@@ -1113,7 +1232,8 @@ template <Variant VAR> constexpr bool kMasked = VAR == Variant::Masked;
 
 template <Variant VAR, int D, StoreMode MODE, bool NEG, bool SLAB_IN, int INSTR = 0>
 static int launch_one(const FwdParams& p, int grid_cap, hipStream_t stream) {
-  const int grid = p.units < grid_cap ? p.units : grid_cap;
+  // A tail round spreads over every slot of the grid.
+  const int grid = p.tail > 0 || p.units >= grid_cap ? grid_cap : p.units;
   hipLaunchKernelGGL((fa_fwd_pp_kernel<D, MODE, NEG, kSplit<VAR>, kMasked<VAR>, SLAB_IN, INSTR>),
                      dim3(grid), dim3(512), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -1181,6 +1301,23 @@ static int launch_instr(int instr, const FwdParams& p, int grid_cap, hipStream_t
     case 2: return launch_one<VAR, 128, StoreMode::Slab, false, false, 2>(p, grid_cap, stream);
     case 3: return launch_one<VAR, 128, StoreMode::Slab, false, false, 3>(p, grid_cap, stream);
   }
+  return -1;
+}
+
+template <int D, StoreMode MODE>
+static int launch_merge_dm(const FwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_merge_kernel<D, MODE>), dim3(p.tail), dim3(512), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_merge(int D, StoreMode mode, const FwdParams& p, hipStream_t stream) {
+  if (p.tail <= 0 || !p.ws) return -1;
+  if (D == 128)
+    return mode == StoreMode::Slab ? launch_merge_dm<128, StoreMode::Slab>(p, stream)
+                                   : launch_merge_dm<128, StoreMode::Plain>(p, stream);
+  if (D == 64)
+    return mode == StoreMode::Slab ? launch_merge_dm<64, StoreMode::Slab>(p, stream)
+                                   : launch_merge_dm<64, StoreMode::Plain>(p, stream);
   return -1;
 }
 

@@ -130,6 +130,45 @@ int relayout_to_slabs_async(const void* plain, void* out_slabs, int B, int H, in
 
 int relayout_to_slabs(const void* plain, void* out_slabs, int B, int H, int S, int D, int P);
 
+/* The dense calls above run the last, partial round of whole 256-query tiles
+ * (when fewer tiles remain than the GPU has resident workgroups) as half
+ * tiles inside each workgroup, which needs no memory beyond the caller's
+ * tensors.  The _ws_ forms instead spread that round over every workgroup:
+ * its tiles form one span of key stages, each workgroup runs an equal slice
+ * of it (a slice meets at most two tiles), writes each tile's partial result
+ * -- output normalised by its own row sum, running max, row sum -- to the
+ * workspace, and a small second launch on the same stream merges the
+ * partials of each tile and stores it like the fused kernel does.  This
+ * balances the persistent owner loop's last round (the schedule the pages'
+ * fused kernels run their tiles in: "Technical Summary: X-Stage in DiT
+ * Inference", Key Contributions 3) instead of leaving CUs idle; the result
+ * equals the other form's within rounding (not bit for bit: the tail tiles'
+ * sums are taken in another order).
+ *   workspace: device memory owned by the caller, 16-byte aligned, at least
+ *   attn_fwd_workspace_bytes(B, H, S, D) bytes for the current device (NULL
+ *   and 0 are accepted when that is 0: masked calls, short sequences and
+ *   calls whose tiles fill whole rounds need none).  Its contents need no
+ *   initialisation and are not meaningful afterwards; calls that may run
+ *   concurrently need separate workspaces.
+ * Status codes as attn_fwd_relayout_async / attn_fwd_plain_async, plus
+ * FA_EINVAL (workspace NULL when one is needed, or workspace_bytes < 0),
+ * FA_EALIGN (workspace not 16-byte aligned) and FA_ERANGE (workspace_bytes
+ * too small), all checked before any kernel is launched. */
+int attn_fwd_relayout_ws_async(const void* q, const void* k, const void* v, void* out_slabs,
+                               int B, int H, int S, int D, int P, float scale,
+                               const uint64_t* mask, void* workspace, int64_t workspace_bytes,
+                               void* stream);
+
+int attn_fwd_plain_ws_async(const void* q, const void* k, const void* v, void* out, int B, int H,
+                            int S, int D, float scale, const uint64_t* mask, void* workspace,
+                            int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace a dense _ws_ call of these sizes needs on the current
+ * device (0 if none), or a negative status: FA_EINVAL (non-positive sizes),
+ * FA_EUNSUPPORTED (D not 64 or 128), FA_ERANGE (sizes beyond the kernel's
+ * index range), FA_EDEVICE (no usable device). */
+int64_t attn_fwd_workspace_bytes(int B, int H, int S, int D);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* attn_status_string(int status);
 
