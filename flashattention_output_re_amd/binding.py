@@ -47,6 +47,7 @@ SIGNATURES = {
                                    ctypes.c_int64, _P],
     "attn_fwd_plain_ws_async": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, ctypes.c_int64, _P],
     "attn_fwd_workspace_bytes": [_I, _I, _I, _I],
+    "attn_fwd_relayout_noalloc_async": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P],
     "attn_status_string": [_I],
     "attn_abi_version": [],
 }
@@ -275,6 +276,21 @@ def attn_fwd_plain_ws_async(q, k, v, out, B, H, S, D, scale, mask=None, workspac
         _nbytes(ws), _stream(stream))
     _raise(st, "attn_fwd_plain_ws_async")
     return ws
+
+
+def attn_fwd_relayout_noalloc_async(q, k, v, out_slabs, B, H, S, D, P, scale, mask=None,
+                                    stream=None):
+    """attn_fwd_relayout_ws_async with the library's static workspace: no
+    device memory is allocated (calls that overlap on one GPU race)."""
+    if P > 0 and S % P == 0:
+        for n, t in (("q", q), ("k", k), ("v", v)):
+            _check_tensor(n, t, (B, H, S, D))
+        _check_tensor("out_slabs", out_slabs, (P, B, S // P, H, D))
+        _check_mask(mask, H, S)
+    st = load_library().attn_fwd_relayout_noalloc_async(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out_slabs), B, H, S, D, P, float(scale), _ptr(mask),
+        _stream(stream))
+    _raise(st, "attn_fwd_relayout_noalloc_async")
 
 
 def attn_instrumented_stamp_words(B: int, H: int, S: int) -> int:

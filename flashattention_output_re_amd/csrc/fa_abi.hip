@@ -301,6 +301,50 @@ int run_relayout(const void* plain, void* out, int B, int H, int S, int D, int P
   return fa::launch_relayout(D, plain, out, rp, grid, stream) == 0 ? FA_OK : FA_ELAUNCH;
 }
 
+// Scratch of the allocation-free entry point: the dense tail round's partial
+// results, two slots per workgroup of a persistent grid of at most 256
+// (seg_floats(128) floats a slot), in a static device array so that the
+// entry point allocates nothing.  Each GPU the library runs on holds its own
+// copy (68 MiB) until the process ends.  Host code never uses the array's
+// name as an address: scratch_address() takes the device address once per
+// device.
+constexpr size_t kScratchFloats = 2 * 256 * (size_t)fa::seg_floats(128);
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, taken with hipGetSymbolAddress
+// on the first call on that device (the device current), or nullptr.
+float* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  return g_scratch_ptr[dev];
+}
+
+// attn_fwd_relayout_ws_async with `scratch` as the workspace.
+int run_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H, int S,
+                int D, int P, float scale, const uint64_t* mask, hipStream_t stream) {
+  fa::FwdParams p;
+  int st = make_params(fa::StoreMode::Slab, q, k, v, out, B, H, S, D, P, scale, mask, false, &p);
+  if (st != FA_OK) return st;
+  DensePlan plan;
+  st = plan_call(D, fa::StoreMode::Slab, mask != nullptr, p, &plan, true);
+  if (st != FA_OK) return st;
+  if (plan.ws_bytes > (int64_t)sizeof(scratch)) return FA_ERANGE;
+  if (plan.ws_bytes > 0) {
+    p.ws = scratch_address();
+    if (!p.ws) return FA_EDEVICE;
+  }
+  return launch_call(D, fa::StoreMode::Slab, p, plan, stream, false, 0);
+}
+
 int finish_blocking(int st) {
   if (st != FA_OK) return st;
   return hipStreamSynchronize(nullptr) == hipSuccess ? FA_OK : FA_EEXEC;
@@ -364,6 +408,13 @@ int attn_fwd_relayout_ws_async(const void* q, const void* k, const void* v, void
                                void* stream) {
   return run_ws(fa::StoreMode::Slab, q, k, v, out_slabs, B, H, S, D, P, scale, mask, workspace,
                 workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_relayout_noalloc_async(const void* q, const void* k, const void* v, void* out_slabs,
+                                    int B, int H, int S, int D, int P, float scale,
+                                    const uint64_t* mask, void* stream) {
+  return run_noalloc(q, k, v, out_slabs, B, H, S, D, P, scale, mask,
+                     static_cast<hipStream_t>(stream));
 }
 
 int attn_fwd_plain_ws_async(const void* q, const void* k, const void* v, void* out, int B, int H,

@@ -163,6 +163,23 @@ int attn_fwd_plain_ws_async(const void* q, const void* k, const void* v, void* o
                             int S, int D, float scale, const uint64_t* mask, void* workspace,
                             int64_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the call of
+ * attn_fwd_relayout_ws_async with the library's own workspace, a static
+ * device array of 68 MiB that every GPU the library runs on holds until the
+ * process ends, so a call needs no memory beyond q, k, v, out_slabs (and the
+ * mask).  Same arguments (no workspace), status codes and result as
+ * attn_fwd_relayout_ws_async; FA_ERANGE when a call would need more than the
+ * array holds (only on GPUs with more than 256 resident workgroups),
+ * FA_EDEVICE when the array's device address cannot be obtained.  Every call
+ * on one GPU shares that GPU's array: calls that may overlap on one GPU
+ * (concurrent streams) race and must not be made; calls ordered on one
+ * stream are safe.  Nothing carries over between calls (each call writes
+ * every workspace slot it reads), so nothing needs clearing. */
+int attn_fwd_relayout_noalloc_async(const void* q, const void* k, const void* v, void* out_slabs,
+                                    int B, int H, int S, int D, int P, float scale,
+                                    const uint64_t* mask, void* stream);
+
 /* Bytes of workspace a dense _ws_ call of these sizes needs on the current
  * device (0 if none), or a negative status: FA_EINVAL (non-positive sizes),
  * FA_EUNSUPPORTED (D not 64 or 128), FA_ERANGE (sizes beyond the kernel's

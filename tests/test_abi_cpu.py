@@ -207,6 +207,18 @@ def test_workspace_query_validation(lib, args, code):
     assert lib.attn_fwd_workspace_bytes(*args) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(S=0), -1), (dict(scale=2.0 ** 70), -1),
+    (dict(S=255, P=2), -2), (dict(D=96), -3), (dict(v=C + 4), -4), (dict(S=(1 << 23), P=1), -5),
+])
+def test_noalloc_validation(lib, kw, code):
+    a = dict(q=A, k=B_, v=C, out=O, Bn=1, H=2, S=4096, D=128, P=2, scale=0.1, mask=None)
+    a.update(kw)
+    assert lib.attn_fwd_relayout_noalloc_async(a["q"], a["k"], a["v"], a["out"], a["Bn"], a["H"],
+                                               a["S"], a["D"], a["P"], a["scale"], a["mask"],
+                                               None) == code
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
 def test_workspace_entries_without_device_report_no_device(lib):
     assert _ws(lib) == -7
