@@ -57,6 +57,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128;          // rows of a mask tile (queries and keys); masked unit size
 constexpr int BN = 64;           // keys per LDS stage
+// Rounds of a masked launch's schedule a workgroup can hold (plain order
+// beyond).
+constexpr int kPlanMaxRounds = 256;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr float kRaise = 256.0f;   // a lane's stage sum that raises the running max
 
 // Tuning knob, overridable at build time (-D): operand reads issued ahead of
@@ -618,6 +622,8 @@ void fa_fwd_pp_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t vb3[NBUF == 4 ? NG : 1][NBUF == 4 ? E : 8];
   // Group 1's running (max, sum) hand-over (split units only).
   __shared__ float ml[SPLIT ? 2 * 256 : 1];
+  // Masked launches: this workgroup's unit in each round of the schedule.
+  __shared__ int plan_col[MASKED ? kPlanMaxRounds : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1010,14 +1016,105 @@ void fa_fwd_pp_kernel(FwdParams p) {
 
   // This workgroup's work items: the launch's units slot, slot + G, ... and
   // then (whole form) its tail segments.  Dense units in XCD-aware order.
-  // Masked units keep the plain order: on a 30%-dense block mask the
-  // XCD-aware order measured slower (its workgroups skip different tiles, so
-  // they do not stream K/V in step as dense tiles do).
+  // Masked units run on the schedule below (plain order beyond its limits):
+  // on a 30%-dense block mask the XCD-aware order measured slower (its
+  // workgroups skip different tiles, so they do not stream K/V in step as
+  // dense tiles do).
   const int G = (int)gridDim.x;
   const int slot = MASKED ? (int)blockIdx.x : xcd_slot(blockIdx.x, G);
-  const int n_units = slot < p.units ? (p.units - slot + G - 1) / G : 0;
+  int n_units = slot < p.units ? (p.units - slot + G - 1) / G : 0;
+  // Masked schedule.  A masked unit's Q-loop time is close to linear in K,
+  // its row's kept tiles, so the plain order -- G units per round -- leaves
+  // the workgroups that drew costly units running after the others.  The
+  // rounds keep the plain order's units (round r holds units r G .. r G +
+  // G - 1, so a round's workgroups still share heads and their K/V), and
+  // within each the units are dealt in decreasing K (ties by index) in snake
+  // order: in even rounds workgroup w takes the w-th costliest, in odd
+  // rounds the (G - 1 - w)-th, so the costly units of one round pair with
+  // the cheap ones of the next.  Every workgroup derives its own column
+  // from the mask alone -- the kept tiles of every mask row (LDS atomics
+  // into kb0, which no DMA has touched yet), then per round a search over K
+  // with wave ballots -- so all agree without any exchange.
+  constexpr int kPlanRows = NG * E / 2;    // int row counts that fit in kb0
+  const int rounds = (p.units + G - 1) / G;
+  const int plan_hn = p.H * p.nmt;          // mask rows
+  const bool planned = MASKED && G <= 256 && rounds <= kPlanMaxRounds && plan_hn <= kPlanRows &&
+                       plan_hn * p.mw < (1 << 24);
+  if constexpr (MASKED) {
+    if (planned) {
+      int* const kept_of = reinterpret_cast<int*>(&kb0[0][0]);   // [mask row]
+      for (int i = tid; i < plan_hn; i += 512) kept_of[i] = 0;
+      __syncthreads();
+      const int nw = plan_hn * p.mw;
+      const float inv_mw = 1.0f / (float)p.mw;
+      const uint64_t last_mask = (p.nmt & 63) ? (1ull << (p.nmt & 63)) - 1 : ~0ull;
+      for (int f0 = 0; f0 < nw; f0 += 512 * 8) {
+        uint64_t wd[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int f = f0 + 512 * j + tid;
+          wd[j] = f < nw ? p.mask[f] : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int f = f0 + 512 * j + tid;
+          // f / mw, exact after one correction (f < 2^24).
+          int row = (int)((float)f * inv_mw);
+          row -= row * p.mw > f;
+          row += (row + 1) * p.mw <= f;
+          const uint64_t x = f - row * p.mw == p.mw - 1 ? wd[j] & last_mask : wd[j];
+          if (f < nw && x) atomicAdd(&kept_of[row], __builtin_popcountll(x));
+        }
+      }
+      __syncthreads();
+      // Wave v finds this workgroup's unit in rounds v, v + 8, ...: the rank
+      // k it takes, the K value c* of that rank (the largest c with more
+      // than k units of K >= c, by bisection), and the unit among those of
+      // K = c*, in index order.
+      for (int r = wave; r < rounds; r += 8) {
+        const int base = r * G;
+        const int nr = p.units - base < G ? p.units - base : G;
+        const int k = (r & 1) ? G - 1 - slot : slot;
+        int unit = -1;
+        if (k < nr) {
+          int kc[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 64 * e + lane;
+            kc[e] = j < nr ? kept_of[(base + j) % plan_hn] : -1;
+          }
+          auto count_ge = [&](int c) FA_INL {
+            int n = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) n += __builtin_popcountll(__ballot(kc[e] >= c));
+            return n;
+          };
+          int lo = 0, hi = p.nmt;   // count_ge(lo) = nr > k
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (count_ge(mid) > k) lo = mid; else hi = mid - 1;
+          }
+          int off = k - count_ge(lo + 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint64_t bits = __ballot(kc[e] == lo);
+            const int n = __builtin_popcountll(bits);
+            if (unit < 0 && off < n) {
+              for (int t = 0; t < off; ++t) bits &= bits - 1;
+              unit = base + 64 * e + __builtin_ctzll(bits);
+            }
+            off -= n;
+          }
+        }
+        if (lane == 0) plan_col[r] = unit;
+      }
+      __syncthreads();
+      n_units = rounds - (plan_col[rounds - 1] < 0 ? 1 : 0);
+    }
+  }
   const int n_items = n_units + tail_segments(slot);
   auto make_item = [&](int i) FA_INL {
+    if (planned) return make_unit(__builtin_amdgcn_readfirstlane(plan_col[i]));
     return i < n_units ? make_unit(slot + i * G) : make_segment(slot, i - n_units);
   };
   if (n_items == 0) return;

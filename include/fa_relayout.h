@@ -34,7 +34,12 @@
  *     [128 j, 128 j + 128) -- takes part iff bit (j % 64) of word j / 64 of
  *     row (h, i) is set.  The same mask applies to every batch index.
  *     Masked tiles contribute nothing to the softmax; a query row whose
- *     tiles are all masked gets an output row of zeros.
+ *     tiles are all masked gets an output row of zeros.  Each 128-query
+ *     tile is one work unit whose time grows with its row's kept tiles;
+ *     each round of units is dealt in decreasing order of kept tiles, in
+ *     alternating directions from round to round (a schedule every
+ *     workgroup derives from the mask), which decides only where a tile is
+ *     computed, never its result.
  *   - Keys at positions >= S do not exist (the ragged last tile is handled);
  *     rows >= S are never written.
  *   - Validation happens before any HIP call: on an error nothing is
