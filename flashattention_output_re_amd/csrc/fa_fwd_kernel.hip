@@ -124,11 +124,23 @@ template <int D> struct Tile {
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int ELEMS = BN * D;               // bf16 per stage
 };
-// K rows are read 16 at a time at one logical chunk: XOR with the row's low bits.
-template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Tile<D>::CH - 1); }
-// V is read by ds_read_b64_tr_b16: 4 consecutive rows at 2 consecutive chunks
-// per 16 lanes; XOR the chunk by 4 * (row % 4).
-template <int D> __device__ __forceinline__ int v_swz(int r) { return (4 * (r & 3)) & (Tile<D>::CH - 1); }
+// LDS: 64 banks of 4 bytes; a ds_read_b128 serves 16 lanes per pass, a
+// ds_read_b64(_tr) 32.  A row of D = 128 (256 bytes) starts at bank 0, one of
+// D = 64 (128 bytes) at bank 0 or 32 by the row's parity.
+// K rows are read 16 at a time (lanes 0-15: rows r0 .. r0 + 15) at one
+// logical chunk: D = 128 XORs the chunk with r % 16, giving 16 distinct
+// 16-byte positions; D = 64 with (r / 2) % 8, distinct within each parity
+// (which picks the half of the banks).
+template <int D> __device__ __forceinline__ int k_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+// V is read by ds_read_b64_tr_b16: per 32 lanes, rows r0 .. r0 + 3 (r0 a
+// multiple of 4) at 4 consecutive logical chunks each; the 4 rows' 64-byte
+// runs must cover all 64 banks.  D = 128: XOR the chunk with 4 (r % 4);
+// D = 64: rows of one parity share a bank half, so XOR with 4 ((r / 2) % 2).
+template <int D> __device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 // LDS-DMA instructions (1 KiB each) that each of four waves issues to move
 // one K or V stage of BN keys.
