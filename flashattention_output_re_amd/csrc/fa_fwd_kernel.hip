@@ -1280,23 +1280,23 @@ void fa_fwd_pp_kernel(FwdParams p) {
   }
 }
 
-// Merge of a dense call's tail round: one workgroup of 8 waves per tail tile,
-// each lane standing where the fused kernel's lane with the same query and
-// dims stood.  The tile's partial results are the workspace slots of the
+// Merge of a dense call's tail round: one workgroup of one wave per tail
+// tile and wave of the fused kernel (blockIdx.y), each lane standing where
+// the fused kernel's lane with the same query and dims stood.  The tile's partial results are the workspace slots of the
 // workgroups whose slice of the tail span [sid L, (sid + 1) L) overlaps its
 // stages [ti ns, (ti + 1) ns): slot 2 sid for the first tile of a slice,
 // 2 sid + 1 for the second.  Each partial holds its output normalised by its
 // own row sum l, taken against its own running max m (log2 domain); with m*
 // the largest m and weights w = 2^(m - m*) l, O = sum w O_part / sum w, the
 // partials taken in slice order, and the tile is rounded and stored like a
-// whole unit's.
+// whole unit's.  The loops over partials are unrolled so that several
+// partials' loads are in flight at once.
 template <int D, StoreMode MODE>
-__global__ __launch_bounds__(512) void fa_merge_kernel(FwdParams p) {
+__global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
   constexpr int NDB = D / 32;
   typedef float f32x4 __attribute__((ext_vector_type(4)));
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x;
+  const int wave = blockIdx.y;
   const int l32 = lane & 31, g = lane >> 5;
   const int ns = (p.S + BN - 1) / BN;
   const int ti = blockIdx.x;
@@ -1309,12 +1309,14 @@ __global__ __launch_bounds__(512) void fa_merge_kernel(FwdParams p) {
     return p.ws + (size_t)(2 * sid + (sid * L / ns == ti ? 0 : 1)) * seg_floats(D);
   };
   float m = -3.0e38f;
+#pragma unroll 4
   for (int sid = w0; sid <= w1; ++sid)
     m = fmaxf(m, reinterpret_cast<const f32x4*>(part(sid) + seg_ml_offset(D))[wave * 64 + lane][0]);
   f32x16 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
   float l = 0.0f;
+#pragma unroll 2
   for (int sid = w0; sid <= w1; ++sid) {
     const float* const ws = part(sid);
     const f32x4 ml = reinterpret_cast<const f32x4*>(ws + seg_ml_offset(D))[wave * 64 + lane];
@@ -1415,7 +1417,7 @@ static int launch_instr(int instr, const FwdParams& p, int grid_cap, hipStream_t
 
 template <int D, StoreMode MODE>
 static int launch_merge_dm(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_merge_kernel<D, MODE>), dim3(p.tail), dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((fa_merge_kernel<D, MODE>), dim3(p.tail, 8), dim3(64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
