@@ -99,13 +99,14 @@ void div_magic(uint32_t d, uint32_t* magic, int* shift) {
 // How one dense call splits into launches: `whole` units of whole 256-query
 // tiles on up to `cap` workgroups, then either (split_units > 0) the last
 // round's tiles as 2 x tail half tiles in a second launch on up to
-// `split_cap`, or (tail > 0, with a workspace) the last round's `tail` tiles
-// as one span of tail * ns stages that the `cap` workgroups of the first
-// launch share in slices of tail_len stages, their partial results merged by
-// a second, small launch.
+// `split_cap`, or (tail > 0, with a workspace) the last round's `tail`
+// tiles shared by the `cap` workgroups of the first launch -- tile i's
+// first tail_len stages on workgroup i, the tiles' remaining stages in
+// slices of tail_hlen on the others -- their partial results merged by a
+// second, small launch.
 struct DensePlan {
   int whole_units = 0, split_units = 0, cap = 0, split_cap = 0;
-  int tail = 0, tail_len = 0;
+  int tail = 0, tail_len = 0, tail_hlen = 0;
   int64_t ws_bytes = 0;    // workspace the tail round needs
 };
 
@@ -137,14 +138,17 @@ int plan_call(int D, fa::StoreMode mode, bool masked, const fa::FwdParams& p, De
   const int stages = (p.S + 63) / 64;
   const int64_t span = (int64_t)tail * stages;
   const int64_t slice = (span + cap - 1) / cap;
-  if (use_ws && tail > 0 && slice >= kTailMinSlice) {
-    // Every slot takes tail_len <= stages stages of the span, so a slice
-    // meets at most two tiles: two workspace slots per slot that has one.
+  if (use_ws && tail > 0 && slice >= kTailMinSlice && slice < stages) {
+    // Each of the cap slots runs about slice stages: tile i's first slice
+    // on slot i, the t (stages - slice) stages of the tiles' ends in equal
+    // slices (no longer than slice) on the cap - t others.  Workspace: one
+    // slot per lead and one per (helper, tile end) piece, tail + cap - 1.
+    const int64_t ends = (int64_t)tail * (stages - slice);
     plan->whole_units = p.units - tail;
     plan->tail = tail;
     plan->tail_len = (int)slice;
-    const int64_t slices = (span + slice - 1) / slice;
-    plan->ws_bytes = 2 * slices * (int64_t)fa::seg_floats(D) * 4;
+    plan->tail_hlen = (int)((ends + (cap - tail) - 1) / (cap - tail));
+    plan->ws_bytes = (int64_t)(tail + cap) * fa::seg_floats(D) * 4;
     return FA_OK;
   }
   if (tail == 0 || 2 * tail > cap || stages < 2) return FA_OK;
@@ -206,6 +210,7 @@ int launch_call(int D, fa::StoreMode mode, const fa::FwdParams& p, const DensePl
     whole.units = plan.whole_units;
     whole.tail = plan.tail;
     whole.tail_len = plan.tail_len;
+    whole.tail_hlen = plan.tail_hlen;
     if (fa::launch_fwd(D, mode, var, whole, plan.cap, stream, slab_in, 0) != 0) return FA_ELAUNCH;
     return fa::launch_merge(D, mode, whole, stream) == 0 ? FA_OK : FA_ELAUNCH;
   }

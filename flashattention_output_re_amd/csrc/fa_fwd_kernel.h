@@ -38,13 +38,14 @@ struct FwdParams {
   // Instrumented launches only: per-unit timestamp records (8 uint32 per
   // unit and wave), else nullptr.
   uint32_t* stamps;
-  // Whole form only: the tail round, run after the launch's `units` whole
-  // units as one span of tail * ns stages (ns = ceil(S / 64)) of the next
-  // `tail` tiles, workgroup slot sid taking [sid * tail_len, (sid + 1) *
-  // tail_len); partial results go to ws (seg_floats(D) floats per slot, two
-  // slots per workgroup) and fa_merge_kernel stores those tiles.  tail = 0:
-  // no tail round.
-  int tail, tail_len;
+  // Whole form only: the tail round, the next `tail` tiles after the
+  // launch's `units` whole units, each split at stage tail_len < ns (ns =
+  // ceil(S / 64)): workgroup slot i < tail runs tile i's stages [0,
+  // tail_len), the other slots equal slices of tail_hlen stages of the tiles'
+  // ends taken one after another.  Partial results go to ws (seg_floats(D)
+  // floats per slot, tail + grid - 1 slots) and fa_merge_kernel stores those
+  // tiles.  tail = 0: no tail round.
+  int tail, tail_len, tail_hlen;
   float* ws;
 };
 

@@ -729,31 +729,51 @@ void fa_fwd_pp_kernel(FwdParams p) {
     return u;
   };
   // Tail segments (whole form): the tail round's t tiles, after the launch's
-  // whole units, are one span of t * ns stages, of which the workgroup in
-  // slot sid runs [sid * L, (sid + 1) * L), L = p.tail_len <= ns: at most two
-  // segments, the end of one tile and the start of the next.  Segment j of
-  // slot sid writes workspace slot 2 sid + j.
+  // whole units, each split at stage L = p.tail_len < ns.  The lead segment
+  // [0, L) of tile i runs on slot i: slots 0 .. t - 1 start together and
+  // stream their tiles' K/V in step, as whole units do (tiles of one head,
+  // an XCD's slots being consecutive).  The ends [L, ns) of the t tiles, one
+  // span of t e stages (e = ns - L) tile by tile, are cut into slices of
+  // Lh = p.tail_hlen <= L stages for the other slots: helper hh = sid - t
+  // runs [hh Lh, (hh + 1) Lh) of the span, one segment per tile end it
+  // meets.  Workspace slots: the lead of tile i writes slot i, helper hh's
+  // piece of tile i slot t + i + hh (distinct, as the helpers' tiles never
+  // go back; below t + G - 1).
   auto tail_segments = [&](int sid) FA_INL {
     if (SPLIT || MASKED || p.tail <= 0) return 0;
-    const int a = sid * p.tail_len;
-    const int b = a + p.tail_len < p.tail * ns ? a + p.tail_len : p.tail * ns;
+    if (sid < p.tail) return 1;
+    const int e = ns - p.tail_len;
+    if (e <= 0) return 0;
+    const int a = (sid - p.tail) * p.tail_hlen;
+    const int b = a + p.tail_hlen < p.tail * e ? a + p.tail_hlen : p.tail * e;
     if (a >= b) return 0;
-    return (b - 1) / ns > a / ns ? 2 : 1;
+    return (b - 1) / e - a / e + 1;
   };
   auto make_segment = [&](int sid, int j) FA_INL {
     Unit u;
-    const int a = sid * p.tail_len;
-    const int b = a + p.tail_len < p.tail * ns ? a + p.tail_len : p.tail * ns;
-    const int ti = a / ns + j;
-    const int st0 = j == 0 ? a - ti * ns : 0;
-    const int st1 = (b < (ti + 1) * ns ? b : (ti + 1) * ns) - ti * ns;
+    int ti, st0, st1, seg;
+    if (sid < p.tail) {
+      ti = sid;
+      st0 = 0;
+      st1 = p.tail_len;
+      seg = sid;
+    } else {
+      const int e = ns - p.tail_len;
+      const int hh = sid - p.tail;
+      const int a = hh * p.tail_hlen;
+      const int b = a + p.tail_hlen < p.tail * e ? a + p.tail_hlen : p.tail * e;
+      ti = a / e + j;
+      st0 = p.tail_len + (j == 0 ? a - ti * e : 0);
+      st1 = p.tail_len + (b < (ti + 1) * e ? b : (ti + 1) * e) - ti * e;
+      seg = p.tail + ti + hh;
+    }
     make_tile(p.units + ti, u);
     u.uidx = -1;
     u.qrow = u.qt * 256 + wave * 32 + l32;
     u.s0 = st0;
     u.nst = st1 - st0;
     u.nloop = st1 - st0;
-    u.seg = 2 * sid + j;
+    u.seg = seg;
     return u;
   };
   // First key of stage j of unit u's stream; a stage past the end is read
@@ -1282,15 +1302,15 @@ void fa_fwd_pp_kernel(FwdParams p) {
 
 // Merge of a dense call's tail round: one workgroup of one wave per tail
 // tile and wave of the fused kernel (blockIdx.y), each lane standing where
-// the fused kernel's lane with the same query and dims stood.  The tile's partial results are the workspace slots of the
-// workgroups whose slice of the tail span [sid L, (sid + 1) L) overlaps its
-// stages [ti ns, (ti + 1) ns): slot 2 sid for the first tile of a slice,
-// 2 sid + 1 for the second.  Each partial holds its output normalised by its
-// own row sum l, taken against its own running max m (log2 domain); with m*
-// the largest m and weights w = 2^(m - m*) l, O = sum w O_part / sum w, the
-// partials taken in slice order, and the tile is rounded and stored like a
-// whole unit's.  The loops over partials are unrolled so that several
-// partials' loads are in flight at once.
+// the fused kernel's lane with the same query and dims stood.  Tile ti's
+// partial results: its lead segment's (workspace slot ti) and those of the
+// helpers hh whose slice [hh Lh, (hh + 1) Lh) of the tile-end span meets
+// [ti e, (ti + 1) e) (slot t + ti + hh).  Each partial holds its output
+// normalised by its own row sum l, taken against its own running max m
+// (log2 domain); with m* the largest m and weights w = 2^(m - m*) l,
+// O = sum w O_part / sum w, the partials taken lead first, then by helper,
+// and the tile is rounded and stored like a whole unit's.  The loops over
+// partials are unrolled so that several partials' loads are in flight.
 template <int D, StoreMode MODE>
 __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
   constexpr int NDB = D / 32;
@@ -1303,22 +1323,24 @@ __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
   const int tile = p.units + ti;
   const int bh = tile / p.nqt, qt = tile - bh * p.nqt;
   const int b = bh / p.H, h = bh - b * p.H;
-  const int L = p.tail_len;
-  const int w0 = ti * ns / L, w1 = ((ti + 1) * ns - 1) / L;
-  auto part = [&](int sid) FA_INL {
-    return p.ws + (size_t)(2 * sid + (sid * L / ns == ti ? 0 : 1)) * seg_floats(D);
+  const int e = ns - p.tail_len, Lh = p.tail_hlen;
+  const int h0 = e > 0 ? ti * e / Lh : 0;
+  const int np = e > 0 ? ((ti + 1) * e - 1) / Lh - h0 + 2 : 1;   // lead + helpers
+  auto part = [&](int k) FA_INL {
+    const int slot = k == 0 ? ti : p.tail + ti + h0 + k - 1;
+    return p.ws + (size_t)slot * seg_floats(D);
   };
   float m = -3.0e38f;
 #pragma unroll 4
-  for (int sid = w0; sid <= w1; ++sid)
-    m = fmaxf(m, reinterpret_cast<const f32x4*>(part(sid) + seg_ml_offset(D))[wave * 64 + lane][0]);
+  for (int k = 0; k < np; ++k)
+    m = fmaxf(m, reinterpret_cast<const f32x4*>(part(k) + seg_ml_offset(D))[wave * 64 + lane][0]);
   f32x16 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
   float l = 0.0f;
 #pragma unroll 2
-  for (int sid = w0; sid <= w1; ++sid) {
-    const float* const ws = part(sid);
+  for (int k = 0; k < np; ++k) {
+    const float* const ws = part(k);
     const f32x4 ml = reinterpret_cast<const f32x4*>(ws + seg_ml_offset(D))[wave * 64 + lane];
     const float a = __builtin_amdgcn_exp2f(ml[0] - m) * ml[1];
     l += a;

@@ -139,11 +139,15 @@ int relayout_to_slabs(const void* plain, void* out_slabs, int B, int H, int S, i
  * (when fewer tiles remain than the GPU has resident workgroups) as half
  * tiles inside each workgroup, which needs no memory beyond the caller's
  * tensors.  The _ws_ forms instead spread that round over every workgroup:
- * its tiles form one span of key stages, each workgroup runs an equal slice
- * of it (a slice meets at most two tiles), writes each tile's partial result
- * -- output normalised by its own row sum, running max, row sum -- to the
- * workspace, and a small second launch on the same stream merges the
- * partials of each tile and stores it like the fused kernel does.  This
+ * each of its t tiles is split at the same key stage L (about t/G of the
+ * tile for G workgroups); workgroup i runs tile i's first L stages -- the t
+ * leads start together and stream each tile's K/V in step, as full rounds
+ * do -- and the other G - t workgroups run equal slices of the tiles'
+ * remaining stages taken one tile after another.  Each piece writes its
+ * partial result -- output normalised by its own row sum, running max, row
+ * sum -- to the workspace, and a small second launch on the same stream
+ * merges the partials of each tile and stores it like the fused kernel
+ * does.  This
  * balances the persistent owner loop's last round (the schedule the pages'
  * fused kernels run their tiles in: "Technical Summary: X-Stage in DiT
  * Inference", Key Contributions 3) instead of leaving CUs idle; the result
