@@ -1077,25 +1077,29 @@ void fa_fwd_pp_kernel(FwdParams p) {
       int* const kept_of = reinterpret_cast<int*>(&kb0[0][0]);   // [mask row]
       for (int i = tid; i < plan_hn; i += 512) kept_of[i] = 0;
       __syncthreads();
+      // Word i of row r is item f = i * rows + r, so a wave's lanes add
+      // into distinct rows' counters.
       const int nw = plan_hn * p.mw;
-      const float inv_mw = 1.0f / (float)p.mw;
+      const float inv_hn = 1.0f / (float)plan_hn;
       const uint64_t last_mask = (p.nmt & 63) ? (1ull << (p.nmt & 63)) - 1 : ~0ull;
       for (int f0 = 0; f0 < nw; f0 += 512 * 8) {
         uint64_t wd[8];
+        int row[8], wi[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int f = f0 + 512 * j + tid;
-          wd[j] = f < nw ? p.mask[f] : 0ull;
+          // f / rows, exact after one correction (f < 2^24).
+          int i = (int)((float)f * inv_hn);
+          i -= i * plan_hn > f;
+          i += (i + 1) * plan_hn <= f;
+          wi[j] = i;
+          row[j] = f - i * plan_hn;
+          wd[j] = f < nw ? p.mask[(size_t)row[j] * p.mw + i] : 0ull;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int f = f0 + 512 * j + tid;
-          // f / mw, exact after one correction (f < 2^24).
-          int row = (int)((float)f * inv_mw);
-          row -= row * p.mw > f;
-          row += (row + 1) * p.mw <= f;
-          const uint64_t x = f - row * p.mw == p.mw - 1 ? wd[j] & last_mask : wd[j];
-          if (f < nw && x) atomicAdd(&kept_of[row], __builtin_popcountll(x));
+          const uint64_t x = wi[j] == p.mw - 1 ? wd[j] & last_mask : wd[j];
+          if (x) atomicAdd(&kept_of[row[j]], __builtin_popcountll(x));
         }
       }
       __syncthreads();
