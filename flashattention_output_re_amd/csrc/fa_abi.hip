@@ -19,7 +19,7 @@ constexpr int kMaxDevices = 64;
 // uint32 words of timestamps per unit of an instrumented launch: one record
 // of 8 words for each of the 8 waves.
 constexpr int kStampWordsPerUnit = 64;
-constexpr float kMaxScale = 18446744073709551616.0f;   // 2^64
+constexpr float kMaxScale = 65536.0f;   // 2^16
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -28,8 +28,13 @@ int validate(const void* q, const void* k, const void* v, const void* out, int B
              int D, int P, float scale, const uint64_t* mask) {
   if (!q || !k || !v || !out) return FA_EINVAL;
   if (B <= 0 || H <= 0 || S <= 0 || P <= 0) return FA_EINVAL;
-  // |scale| <= 2^64 keeps scale * log2(e) * score inside fp32 for every
-  // score below 2^62 in magnitude; larger scales are rejected.
+  // The kernel takes each weight as exp2(fma(s, c, -m)), c = scale * log2(e),
+  // m = the rounded product of the row's largest score: the row's weights
+  // share the factor exp2(rounding error of m), which cancels in the
+  // normalisation while |s * c| < 2^24 (the factor stays within [1/2, 2]);
+  // |scale| <= 2^16 keeps that for every score up to 2^7.5 in magnitude, and
+  // larger scales are rejected.  (Far beyond, at |s * c| near 2^31 and up,
+  // the factor would leave fp32's range.)
   if (!std::isfinite(scale) || std::fabs(scale) > kMaxScale) return FA_EINVAL;
   if (D != 64 && D != 128) return FA_EUNSUPPORTED;
   if (S % P != 0) return FA_EDIV;
@@ -479,7 +484,7 @@ const char* attn_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_EINVAL:
-      return "invalid argument (null tensor, non-positive size, or scale not finite or beyond 2^64)";
+      return "invalid argument (null tensor, non-positive size, or scale not finite or beyond 2^16)";
     case FA_EDIV: return "S is not a multiple of the slab count P";
     case FA_EUNSUPPORTED:
       return "unsupported shape (D must be 64 or 128; slab inputs need S/P >= 64)";

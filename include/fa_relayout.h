@@ -25,9 +25,12 @@
  *     occupancy; calls on different streams may run concurrently.
  *   - q, k, v: bf16 [B][H][S][D], contiguous, 16-byte aligned.
  *   - scale: multiplies Q K^T before the softmax; any finite value with
- *     |scale| <= 2^64 (0 gives the mean of V; negative values are allowed).
- *     The kernel forms scale * log2(e) * (q . k) in fp32, so scores must keep
- *     that product finite (|q . k| < 2^62 at the largest scale).
+ *     |scale| <= 2^16 (0 gives the mean of V; negative values are allowed).
+ *     The kernel forms scale * log2(e) * (q . k) in fp32; results meet the
+ *     error bound of bf16 attention while that product stays below 2^24 in
+ *     magnitude for every score (|q . k| < 2^7.5 at |scale| = 2^16, any
+ *     score of unit-variance bf16 inputs at the usual 1/sqrt(D)).  Larger
+ *     products are outside the contract, like NaN or Inf inputs.
  *   - mask: NULL for dense attention, else a device array of uint64 words
  *     [H][nT][W] with nT = ceil(S/128), W = ceil(nT/64), 8-byte aligned.
  *     Tile (i, j) of head h -- queries [128 i, 128 i + 128) against keys
@@ -63,7 +66,7 @@ extern "C" {
 #endif
 
 #define FA_OK 0
-#define FA_EINVAL (-1)        /* null q/k/v/out; B, H, S or P <= 0; scale not finite or > 2^64 */
+#define FA_EINVAL (-1)        /* null q/k/v/out; B, H, S or P <= 0; scale not finite or > 2^16 */
 #define FA_EDIV (-2)          /* S is not a multiple of P */
 #define FA_EUNSUPPORTED (-3)  /* D is not 64 or 128 (slab inputs: S/P < 64) */
 #define FA_EALIGN (-4)        /* a tensor pointer not 16-byte aligned, mask not 8 */
