@@ -39,9 +39,11 @@
 // The probabilities are first taken against the running max as it stands; it
 // is only raised, and the stage recomputed, when some lane's sum over the
 // stage passes kRaise = 2^8.  So no probability exceeds 2^8, and a key that
-// comes to dominate its row is re-centred to weigh exactly 1 (its bf16
-// rounding is then exact).  The final division by the row sum makes the
-// result independent of which max was used.
+// comes to dominate its row is re-centred to weigh 1: exactly 2^e with e the
+// rounding error of its product s c (the max is that rounded product, the
+// probability an fma), which rounds to 1 in bf16 while |s c| < 2^16.  The
+// final division by the row sum makes the result independent of which max
+// was used, the factor 2^e included.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
