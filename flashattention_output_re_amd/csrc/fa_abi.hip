@@ -3,6 +3,7 @@
 // declared in include/fa_relayout.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -112,6 +113,9 @@ void div_magic(uint32_t d, uint32_t* magic, int* shift) {
 struct DensePlan {
   int whole_units = 0, split_units = 0, cap = 0, split_cap = 0;
   int tail = 0, tail_len = 0, tail_hlen = 0;
+  int split_pieces = 0;    // > 1: each half tile cut into that many key pieces
+  // Tiles of the split launch (two half tiles each, in split_pieces pieces).
+  int tail_tiles() const { return split_units / (2 * (split_pieces > 1 ? split_pieces : 1)); }
   int64_t ws_bytes = 0;    // workspace the tail round needs
 };
 
@@ -122,6 +126,9 @@ struct DensePlan {
 // the split half tiles); shorter slices keep the schedule without a
 // workspace.
 constexpr int kTailMinSlice = 64;
+// The shortest piece (in 64-key stages, both groups together) a half tile
+// is cut into when the split launch is spread over a workspace.
+constexpr int kMinPieceStages = 16;
 
 // Launch geometry of a call with params p (units = every tile): the number
 // of units per launch and the persistent grid caps, or FA_EDEVICE.
@@ -162,6 +169,15 @@ int plan_call(int D, fa::StoreMode mode, bool masked, const fa::FwdParams& p, De
   plan->whole_units = p.units - tail;
   plan->split_units = 2 * tail;
   plan->split_cap = split_cap;
+  // With a workspace, half tiles that leave most workgroups idle are cut
+  // into pieces of at least kMinPieceStages key stages, one per workgroup,
+  // merged by a second launch.
+  const int pieces = std::min(split_cap / (2 * tail), stages / kMinPieceStages);
+  if (use_ws && pieces >= 2) {
+    plan->split_pieces = pieces;
+    plan->split_units = 2 * tail * pieces;
+    plan->ws_bytes = (int64_t)plan->split_units * fa::seg_floats(D) * 4;
+  }
   return FA_OK;
 }
 
@@ -228,10 +244,16 @@ int launch_call(int D, fa::StoreMode mode, const fa::FwdParams& p, const DensePl
   if (plan.split_units > 0) {
     fa::FwdParams half = p;
     half.units = plan.split_units;
-    half.unit_base = p.units - plan.split_units / 2;
+    half.unit_base = p.units - plan.tail_tiles();
     if (instr) half.stamps = p.stamps + (size_t)plan.whole_units * kStampWordsPerUnit;
+    if (plan.split_pieces > 1) {
+      if (!p.ws || instr) return FA_ELAUNCH;
+      half.split_pieces = plan.split_pieces;
+    }
     if (fa::launch_fwd(D, mode, fa::Variant::Split, half, plan.split_cap, stream, slab_in,
                        instr) != 0)
+      return FA_ELAUNCH;
+    if (plan.split_pieces > 1 && fa::launch_merge_split(D, mode, half, stream) != 0)
       return FA_ELAUNCH;
   }
   return FA_OK;

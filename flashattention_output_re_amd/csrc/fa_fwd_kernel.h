@@ -47,6 +47,11 @@ struct FwdParams {
   // tiles.  tail = 0: no tail round.
   int tail, tail_len, tail_hlen;
   float* ws;
+  // Split form only: when > 1, each half tile is cut into split_pieces
+  // pieces of its key stages, unit u being piece u % split_pieces of half
+  // unit_base * 2 + u / split_pieces; the pieces' partial results go to ws
+  // slot u and fa_merge_split_kernel stores the half tiles.
+  int split_pieces;
 };
 
 // Workspace slot of one tail segment, in floats: per wave (8) and lane (64)
@@ -68,6 +73,9 @@ int launch_fwd(int D, StoreMode mode, Variant var, const FwdParams& p, int grid_
 // The merge kernel of a call's tail round (p.tail tiles, p.ws), on the
 // stream after the whole-form launch that wrote the partials; 0 on success.
 int launch_merge(int D, StoreMode mode, const FwdParams& p, hipStream_t stream);
+// The merge of a split launch cut into pieces (p.split_pieces > 1, p.units
+// pieces, p.ws), on the stream after that launch; 0 on success.
+int launch_merge_split(int D, StoreMode mode, const FwdParams& p, hipStream_t stream);
 // Resident workgroups per CU for the instance (D, mode, var); 0 on success.
 int kernel_occupancy(int D, StoreMode mode, Variant var, int* blocks_per_cu);
 

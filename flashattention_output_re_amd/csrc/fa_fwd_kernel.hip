@@ -719,6 +719,23 @@ void fa_fwd_pp_kernel(FwdParams p) {
   };
   auto make_unit = [&](int unit) FA_INL {
     Unit u;
+    if (SPLIT && !MASKED && p.split_pieces > 1) {
+      // Piece j of half tile hf: stages [a, b) of its ns, the first half
+      // (rounded up) on group 0, the rest on group 1; its partial result
+      // goes to workspace slot `unit`.
+      const int hf = unit / p.split_pieces, j = unit - hf * p.split_pieces;
+      make_tile(p.unit_base + (hf >> 1), u);
+      u.uidx = unit;
+      u.qrow = u.qt * 256 + (hf & 1) * 128 + wq * 32 + l32;
+      const int ps = (ns + p.split_pieces - 1) / p.split_pieces;
+      const int a = j * ps, b = a + ps < ns ? a + ps : ns;
+      const int hs = (b - a + 1) / 2;
+      u.s0 = a + own * hs;
+      u.nst = own == 0 ? hs : (b - a) - hs;
+      u.nloop = hs;
+      u.seg = unit;
+      return u;
+    }
     make_tile(MASKED ? unit : SPLIT ? p.unit_base + (unit >> 1) : unit, u);
     u.uidx = unit;
     u.qrow = MASKED  ? u.qt * BM + wq * 32 + l32
@@ -1220,6 +1237,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
           for (int r = 0; r < 16; ++r)
             acc[db][r] = acc[db][r] * ax + area[(db * 16 + r) * 64 + lane] * ay;
         l_run = l_run * ax + l_y * ay;
+        m_run = m;
       }
       // Group 0 has read the hand-over area before the next unit's prologue
       // refills stream 0's buffers.
@@ -1275,14 +1293,16 @@ void fa_fwd_pp_kernel(FwdParams p) {
         wait_vm<nst>();
     };
     // Whole units: every wave stores its 32 queries.  Split units: group 0
-    // stores the merged tile, group 1 nothing.  Tail segments: every wave
-    // writes its partial result -- the O^T accumulator normalised by its own
-    // row sum (the same products store_rows forms, so the accumulator is
-    // not kept twice), its running max and that row sum -- to workspace slot
-    // cur.seg for the merge kernel (layout: seg_floats).
+    // stores the merged tile, group 1 nothing.  Tail segments and the pieces
+    // of a split launch cut into pieces: every storing wave (all eight, or
+    // group 0 after the groups' merge) writes its partial result -- the O^T
+    // accumulator normalised by its own row sum (the same products
+    // store_rows forms, so the accumulator is not kept twice), its running
+    // max and that row sum -- to workspace slot cur.seg for the merge kernel
+    // (layout: seg_floats, wave w's part at w).
     if (SPLIT && grp == 1) {
       finish(std::integral_constant<int, 0>{});
-    } else if (!SPLIT && !MASKED && cur.seg >= 0) {
+    } else if (!MASKED && cur.seg >= 0) {
       float* const ws = p.ws + (size_t)cur.seg * seg_floats(D);
       typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -1306,6 +1326,52 @@ void fa_fwd_pp_kernel(FwdParams p) {
   }
 }
 
+// One wave's share (32 queries x D dims) of np partial results, workspace
+// slots slot(0) .. slot(np - 1), combined into acc (unnormalised) and l:
+// online over chunks of up to four partials, each chunk's loads all issued
+// before any is used.  With m the largest running max so far, partial k
+// weighs 2^(m_k - m) l_k, and what is summed is rescaled when m grows.
+template <int D, class Slot>
+__device__ __forceinline__ void merge_partials(const float* ws, int np, const Slot& slot, int wave,
+                                               int lane, f32x16 (&acc)[D / 32], float& l) {
+  constexpr int NDB = D / 32, NQ = 4 * NDB;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+  l = 0.0f;
+  float m = -3.0e38f;
+  for (int k0 = 0; k0 < np; k0 += 4) {
+    f32x4 ml[4], o[4][NQ];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // Past np, partial np - 1 again, weighed 0.
+      const float* const w = ws + (size_t)slot(k0 + j < np ? k0 + j : np - 1) * seg_floats(D);
+      ml[j] = reinterpret_cast<const f32x4*>(w + seg_ml_offset(D))[wave * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) o[j][q] = reinterpret_cast<const f32x4*>(w)[(wave * NQ + q) * 64 + lane];
+    }
+    float mc = m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k0 + j < np) mc = fmaxf(mc, ml[j][0]);
+    const float sc = __builtin_amdgcn_exp2f(m - mc);
+    l *= sc;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[i] *= sc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = k0 + j < np ? __builtin_amdgcn_exp2f(ml[j][0] - mc) * ml[j][1] : 0.0f;
+      l += a;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[q / 4][4 * (q % 4) + c] = __builtin_fmaf(a, o[j][q][c], acc[q / 4][4 * (q % 4) + c]);
+    }
+    m = mc;
+  }
+}
+
 // Merge of a dense call's tail round: one workgroup of one wave per tail
 // tile and wave of the fused kernel (blockIdx.y), each lane standing where
 // the fused kernel's lane with the same query and dims stood.  Tile ti's
@@ -1315,8 +1381,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
 // normalised by its own row sum l, taken against its own running max m
 // (log2 domain); with m* the largest m and weights w = 2^(m - m*) l,
 // O = sum w O_part / sum w, the partials taken lead first, then by helper,
-// and the tile is rounded and stored like a whole unit's.  The loops over
-// partials are unrolled so that several partials' loads are in flight.
+// and the tile is rounded and stored like a whole unit's (merge_partials).
 template <int D, StoreMode MODE>
 __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
   constexpr int NDB = D / 32;
@@ -1332,37 +1397,39 @@ __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
   const int e = ns - p.tail_len, Lh = p.tail_hlen;
   const int h0 = e > 0 ? ti * e / Lh : 0;
   const int np = e > 0 ? ((ti + 1) * e - 1) / Lh - h0 + 2 : 1;   // lead + helpers
-  auto part = [&](int k) FA_INL {
-    const int slot = k == 0 ? ti : p.tail + ti + h0 + k - 1;
-    return p.ws + (size_t)slot * seg_floats(D);
-  };
-  float m = -3.0e38f;
-#pragma unroll 4
-  for (int k = 0; k < np; ++k)
-    m = fmaxf(m, reinterpret_cast<const f32x4*>(part(k) + seg_ml_offset(D))[wave * 64 + lane][0]);
+  auto slot = [&](int k) { return k == 0 ? ti : p.tail + ti + h0 + k - 1; };
   f32x16 acc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-  float l = 0.0f;
-#pragma unroll 2
-  for (int k = 0; k < np; ++k) {
-    const float* const ws = part(k);
-    const f32x4 ml = reinterpret_cast<const f32x4*>(ws + seg_ml_offset(D))[wave * 64 + lane];
-    const float a = __builtin_amdgcn_exp2f(ml[0] - m) * ml[1];
-    l += a;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f32x4 o =
-            reinterpret_cast<const f32x4*>(ws)[(wave * 4 * NDB + db * 4 + rr) * 64 + lane];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[db][4 * rr + k] = __builtin_fmaf(a, o[k], acc[db][4 * rr + k]);
-      }
-  }
+  float l;
+  merge_partials<D>(p.ws, np, slot, wave, lane, acc, l);
   // l is already the whole row's (each partial's sum covers both wave halves).
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   store_rows<D, MODE, NDB>(p, acc, inv, qt * 256 + wave * 32 + l32, 0, b, h, bh, g, lane);
+}
+
+// Merge of a split launch cut into pieces: one workgroup of one wave per half
+// tile and group-0 wave (blockIdx.y), each lane where that wave's lane stood.
+// Half tile hf's pieces are the workspace slots hf * pieces + j; they are
+// combined as in fa_merge_kernel and the half tile is stored like a split
+// unit's.
+template <int D, StoreMode MODE>
+__global__ __launch_bounds__(64) void fa_merge_split_kernel(FwdParams p) {
+  constexpr int NDB = D / 32;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x;
+  const int wave = blockIdx.y;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int hf = blockIdx.x;
+  const int tile = p.unit_base + (hf >> 1);
+  const int bh = tile / p.nqt, qt = tile - bh * p.nqt;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int np = p.split_pieces;
+  auto slot = [&](int k) { return hf * np + k; };
+  f32x16 acc[NDB];
+  float l;
+  merge_partials<D>(p.ws, np, slot, wave, lane, acc, l);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  store_rows<D, MODE, NDB>(p, acc, inv, qt * 256 + (hf & 1) * 128 + wave * 32 + l32, 0, b, h, bh,
+                           g, lane);
 }
 
 // Kernel form of each variant: split-key units, masked units.
@@ -1447,6 +1514,24 @@ template <int D, StoreMode MODE>
 static int launch_merge_dm(const FwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((fa_merge_kernel<D, MODE>), dim3(p.tail, 8), dim3(64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int D, StoreMode MODE>
+static int launch_merge_split_dm(const FwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_merge_split_kernel<D, MODE>), dim3(p.units / p.split_pieces, 4),
+                     dim3(64), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_merge_split(int D, StoreMode mode, const FwdParams& p, hipStream_t stream) {
+  if (p.split_pieces <= 1 || !p.ws || p.units % p.split_pieces != 0) return -1;
+  if (D == 128)
+    return mode == StoreMode::Slab ? launch_merge_split_dm<128, StoreMode::Slab>(p, stream)
+                                   : launch_merge_split_dm<128, StoreMode::Plain>(p, stream);
+  if (D == 64)
+    return mode == StoreMode::Slab ? launch_merge_split_dm<64, StoreMode::Slab>(p, stream)
+                                   : launch_merge_split_dm<64, StoreMode::Plain>(p, stream);
+  return -1;
 }
 
 int launch_merge(int D, StoreMode mode, const FwdParams& p, hipStream_t stream) {

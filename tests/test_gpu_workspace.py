@@ -58,12 +58,18 @@ def run_plain_ws(q, k, v, scale, mask=None):
 
 
 # (B, H, S, D, P) from the CU count n (slice lengths for 256 CUs).  The tail
-# round is spread only when a slice holds at least 64 stages.
+# round is spread as whole-tile pieces when a slice holds at least 64 stages;
+# shorter tails run as half tiles, cut into key pieces of at least 16 stages
+# when that leaves workgroups idle.
 SHAPES = {
     "all tail, slices on tile bounds": lambda n: (1, 1, 16384, 128, 2),        # L = 64
     "all tail, unaligned slices, ragged S": lambda n: (1, 1, 20000, 128, 8),   # L = 97
     "whole round + tail, unaligned": lambda n: (1, 5, 20000, 128, 4),          # L = 170
     "all tail, D=64, B=2": lambda n: (2, 1, 20000, 64, 4),                     # L = 194
+    "half tiles in 2 pieces (Image share)": lambda n: (1, 3, 4096, 128, 8),
+    "half tiles in 4 pieces": lambda n: (1, 1, 4096, 128, 2),
+    "half tiles in 2 pieces, D=64, B=2, ragged S": lambda n: (2, 1, 3000, 64, 4),
+    "whole rounds + half tiles in pieces": lambda n: (1, n + 3, 2048, 128, 4),
 }
 
 
@@ -177,17 +183,17 @@ def test_ws_rejects_small_or_misaligned_workspace():
     assert bool((out == CANARY).all()), "a rejected call wrote its output"
     assert lib.attn_fwd_relayout_ws_async(*args, ws.data_ptr(), need, s) == 0
     torch.cuda.synchronize()
-    # Sizes that fill whole rounds, or whose slices would be short (the
-    # Image share), need no workspace and run as without one.
+    # Sizes that fill whole rounds need no workspace and run as without one;
+    # the Image share's half tiles, cut into pieces, need one.
     n = _cus()
     assert binding.attn_fwd_workspace_bytes(1, n, 256, 128) == 0
-    assert binding.attn_fwd_workspace_bytes(1, 3, 4096, 128) == 0
-    a = torch.empty((8, 1, 512, 3, 128), dtype=torch.bfloat16, device=q.device)
+    assert binding.attn_fwd_workspace_bytes(1, 3, 4096, 128) > 0
+    a = torch.empty((8, 1, 256, n, 128), dtype=torch.bfloat16, device=q.device)
     b = torch.empty_like(a)
-    qi, ki, vi = (to_dev(t) for t in wl.random_qkv(1, 3, 4096, 128, seed=8))
-    fa.attn_fwd_relayout_ws_async(qi, ki, vi, a, 1, 3, 4096, 128, 8, 0.1, None,
+    qi, ki, vi = (to_dev(t) for t in wl.random_qkv(1, n, 2048, 128, seed=8))
+    fa.attn_fwd_relayout_ws_async(qi, ki, vi, a, 1, n, 2048, 128, 8, 0.1, None,
                                   torch.empty(16, dtype=torch.uint8, device=q.device))
-    fa.attn_fwd_relayout_async(qi, ki, vi, b, 1, 3, 4096, 128, 8, 0.1, None)
+    fa.attn_fwd_relayout_async(qi, ki, vi, b, 1, n, 2048, 128, 8, 0.1, None)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
