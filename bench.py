@@ -600,8 +600,12 @@ def main():
     slabs3 = torch.empty_like(slabs)
 
     def slab_in():
-        fa.attn_fwd_slab_to_slab_async(qs, ks, vs, slabs3, w.B, w.H, w.S, w.D, w.P, w.scale, mask,
-                                       stream)
+        if a.no_workspace:
+            fa.attn_fwd_slab_to_slab_async(qs, ks, vs, slabs3, w.B, w.H, w.S, w.D, w.P, w.scale,
+                                           mask, stream)
+        else:
+            fa.attn_fwd_slab_to_slab_ws_async(qs, ks, vs, slabs3, w.B, w.H, w.S, w.D, w.P,
+                                              w.scale, mask, ws, stream)
 
     for _ in range(2):
         slab_in()
@@ -698,8 +702,9 @@ def main():
         "also": also,
         "workspace_bytes": ws_bytes,
         "slab_to_slab": {
-            "what": "attn_fwd_slab_to_slab: q, k, v read from [P][B][S/P][H][D] slabs (the "
-                    "pre-attention exchange fused into the loads) and the output stored into slabs",
+            "what": "attn_fwd_slab_to_slab (its _ws_ form unless --no-workspace): q, k, v read "
+                    "from [P][B][S/P][H][D] slabs (the pre-attention exchange fused into the "
+                    "loads) and the output stored into slabs",
             "median_ms": round(med_s2s, 4),
             "TFLOPs": round(flop / (med_s2s * 1e-3) / 1e12, 2),
             "overhead_vs_fused_pct": round((med_s2s / med_ref - 1.0) * 100.0, 2),

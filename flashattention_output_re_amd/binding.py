@@ -35,6 +35,8 @@ SIGNATURES = {
     "attn_fwd_relayout": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
     "attn_fwd_slab_to_slab_async": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P],
     "attn_fwd_slab_to_slab": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P],
+    "attn_fwd_slab_to_slab_ws_async": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P,
+                                       ctypes.c_int64, _P],
     "attn_fwd_plain_async": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P],
     "attn_fwd_plain": [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P],
     "relayout_to_slabs_async": [_P, _P, _I, _I, _I, _I, _I, _P],
@@ -170,6 +172,24 @@ def attn_fwd_slab_to_slab_async(q_slabs, k_slabs, v_slabs, out_slabs, B, H, S, D
         _ptr(q_slabs), _ptr(k_slabs), _ptr(v_slabs), _ptr(out_slabs), B, H, S, D, P, float(scale),
         _ptr(mask), _stream(stream))
     _raise(st, "attn_fwd_slab_to_slab_async")
+
+
+def attn_fwd_slab_to_slab_ws_async(q_slabs, k_slabs, v_slabs, out_slabs, B, H, S, D, P, scale,
+                                   mask=None, workspace=None, stream=None):
+    """attn_fwd_slab_to_slab_async with the last round spread over every
+    workgroup; workspace as for attn_fwd_relayout_ws_async (allocated here
+    when None)."""
+    if P > 0 and S % P == 0:
+        for n, t in (("q_slabs", q_slabs), ("k_slabs", k_slabs), ("v_slabs", v_slabs),
+                     ("out_slabs", out_slabs)):
+            _check_tensor(n, t, (P, B, S // P, H, D))
+        _check_mask(mask, H, S)
+    ws = _workspace(workspace, B, H, S, D, q_slabs.device)
+    st = load_library().attn_fwd_slab_to_slab_ws_async(
+        _ptr(q_slabs), _ptr(k_slabs), _ptr(v_slabs), _ptr(out_slabs), B, H, S, D, P, float(scale),
+        _ptr(mask), _ptr(ws), _nbytes(ws), _stream(stream))
+    _raise(st, "attn_fwd_slab_to_slab_ws_async")
+    return ws
 
 
 def attn_fwd_slab_to_slab(q_slabs, k_slabs, v_slabs, out_slabs, B, H, S, D, P, scale, mask=None):

@@ -285,9 +285,9 @@ int check_workspace(const void* ws, int64_t ws_bytes, int64_t need) {
 // Masked calls need no workspace and run as without one.
 int run_ws(fa::StoreMode mode, const void* q, const void* k, const void* v, void* out, int B,
            int H, int S, int D, int P, float scale, const uint64_t* mask, void* ws,
-           int64_t ws_bytes, hipStream_t stream) {
+           int64_t ws_bytes, hipStream_t stream, bool slab_in = false) {
   fa::FwdParams p;
-  int st = make_params(mode, q, k, v, out, B, H, S, D, P, scale, mask, false, &p);
+  int st = make_params(mode, q, k, v, out, B, H, S, D, P, scale, mask, slab_in, &p);
   if (st != FA_OK) return st;
   if (ws_bytes < 0) return FA_EINVAL;
   DensePlan plan;
@@ -296,7 +296,7 @@ int run_ws(fa::StoreMode mode, const void* q, const void* k, const void* v, void
   st = check_workspace(ws, ws_bytes, plan.ws_bytes);
   if (st != FA_OK) return st;
   p.ws = static_cast<float*>(ws);
-  return launch_call(D, mode, p, plan, stream, false, 0);
+  return launch_call(D, mode, p, plan, stream, slab_in, 0);
 }
 
 int validate_relayout(const void* plain, const void* out, int B, int H, int S, int D, int P) {
@@ -447,6 +447,14 @@ int attn_fwd_relayout_noalloc_async(const void* q, const void* k, const void* v,
                                     const uint64_t* mask, void* stream) {
   return run_noalloc(q, k, v, out_slabs, B, H, S, D, P, scale, mask,
                      static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_slab_to_slab_ws_async(const void* q_slabs, const void* k_slabs, const void* v_slabs,
+                                   void* out_slabs, int B, int H, int S, int D, int P,
+                                   float scale, const uint64_t* mask, void* workspace,
+                                   int64_t workspace_bytes, void* stream) {
+  return run_ws(fa::StoreMode::Slab, q_slabs, k_slabs, v_slabs, out_slabs, B, H, S, D, P, scale,
+                mask, workspace, workspace_bytes, static_cast<hipStream_t>(stream), true);
 }
 
 int attn_fwd_plain_ws_async(const void* q, const void* k, const void* v, void* out, int B, int H,

@@ -1385,7 +1385,6 @@ __device__ __forceinline__ void merge_partials(const float* ws, int np, const Sl
 template <int D, StoreMode MODE>
 __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
   constexpr int NDB = D / 32;
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x;
   const int wave = blockIdx.y;
   const int l32 = lane & 31, g = lane >> 5;
@@ -1414,7 +1413,6 @@ __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
 template <int D, StoreMode MODE>
 __global__ __launch_bounds__(64) void fa_merge_split_kernel(FwdParams p) {
   constexpr int NDB = D / 32;
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x;
   const int wave = blockIdx.y;
   const int l32 = lane & 31, g = lane >> 5;

@@ -150,16 +150,18 @@ int relayout_to_slabs(const void* plain, void* out_slabs, int B, int H, int S, i
  * partial result -- output normalised by its own row sum, running max, row
  * sum -- to the workspace, and a small second launch on the same stream
  * merges the partials of each tile and stores it like the fused kernel
- * does.  This
- * balances the persistent owner loop's last round (the schedule the pages'
+ * does.  When that share L would be under 64 stages, the round runs as half
+ * tiles as above, each cut into key pieces of at least 16 stages, one per
+ * workgroup, merged the same way.  This balances the persistent owner
+ * loop's last round (the schedule the pages'
  * fused kernels run their tiles in: "Technical Summary: X-Stage in DiT
  * Inference", Key Contributions 3) instead of leaving CUs idle; the result
  * equals the other form's within rounding (not bit for bit: the tail tiles'
  * sums are taken in another order).
  *   workspace: device memory owned by the caller, 16-byte aligned, at least
  *   attn_fwd_workspace_bytes(B, H, S, D) bytes for the current device (NULL
- *   and 0 are accepted when that is 0: masked calls, short sequences and
- *   calls whose tiles fill whole rounds need none).  Its contents need no
+ *   and 0 are accepted when that is 0: masked calls and calls whose tiles
+ *   fill whole rounds need none).  Its contents need no
  *   initialisation and are not meaningful afterwards; calls that may run
  *   concurrently need separate workspaces.
  * Status codes as attn_fwd_relayout_async / attn_fwd_plain_async, plus
@@ -174,6 +176,16 @@ int attn_fwd_relayout_ws_async(const void* q, const void* k, const void* v, void
 int attn_fwd_plain_ws_async(const void* q, const void* k, const void* v, void* out, int B, int H,
                             int S, int D, float scale, const uint64_t* mask, void* workspace,
                             int64_t workspace_bytes, void* stream);
+
+/* attn_fwd_slab_to_slab_async with the last round spread as above: inputs
+ * and output in the slab layout, workspace as for attn_fwd_relayout_ws_async
+ * (attn_fwd_workspace_bytes gives the size).  Its result equals
+ * attn_fwd_relayout_ws_async on the same Q, K, V in [B][H][S][D] bit for
+ * bit.  Status codes as attn_fwd_slab_to_slab plus the workspace's. */
+int attn_fwd_slab_to_slab_ws_async(const void* q_slabs, const void* k_slabs, const void* v_slabs,
+                                   void* out_slabs, int B, int H, int S, int D, int P,
+                                   float scale, const uint64_t* mask, void* workspace,
+                                   int64_t workspace_bytes, void* stream);
 
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation: the call of

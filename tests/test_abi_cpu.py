@@ -186,9 +186,12 @@ def test_instrumented_validation(lib, kw, code):
 
 
 def _ws(lib, q=A, k=B_, v=C, out=O, Bn=1, H=2, S=4096, D=128, P=2, scale=0.1, mask=None,
-        ws=0x70000, nbytes=1 << 30, plain=False):
+        ws=0x70000, nbytes=1 << 30, plain=False, s2s=False):
     if plain:
         return lib.attn_fwd_plain_ws_async(q, k, v, out, Bn, H, S, D, scale, mask, ws, nbytes, None)
+    if s2s:
+        return lib.attn_fwd_slab_to_slab_ws_async(q, k, v, out, Bn, H, S, D, P, scale, mask, ws,
+                                                  nbytes, None)
     return lib.attn_fwd_relayout_ws_async(q, k, v, out, Bn, H, S, D, P, scale, mask, ws, nbytes,
                                           None)
 
@@ -197,6 +200,8 @@ def _ws(lib, q=A, k=B_, v=C, out=O, Bn=1, H=2, S=4096, D=128, P=2, scale=0.1, ma
     (dict(q=None), -1), (dict(out=None), -1), (dict(Bn=0), -1), (dict(scale=math.nan), -1),
     (dict(nbytes=-1), -1), (dict(S=255, P=2), -2), (dict(D=96), -3), (dict(k=B_ + 8), -4),
     (dict(S=(1 << 23), P=1), -5), (dict(plain=True, D=32), -3), (dict(plain=True, v=None), -1),
+    (dict(s2s=True, q=None), -1), (dict(s2s=True, S=256, P=8), -3), (dict(s2s=True, S=255, P=2), -2),
+    (dict(s2s=True, nbytes=-1), -1), (dict(s2s=True, k=B_ + 8), -4),
 ])
 def test_workspace_entry_validation(lib, kw, code):
     assert _ws(lib, **kw) == code
@@ -224,6 +229,7 @@ def test_noalloc_validation(lib, kw, code):
 def test_workspace_entries_without_device_report_no_device(lib):
     assert _ws(lib) == -7
     assert _ws(lib, plain=True) == -7
+    assert _ws(lib, s2s=True) == -7
     assert lib.attn_fwd_workspace_bytes(1, 5, 75600, 128) == -7
 
 

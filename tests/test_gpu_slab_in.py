@@ -107,3 +107,42 @@ def test_slab_inputs_blocking_entry_point():
     fa.attn_fwd_slab_to_slab(qs, ks, vs, a, B, H, S, D, P, 0.125)
     b = run_slabs(to_dev(q), to_dev(k), to_dev(v), P, 0.125)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+WS_CASES = {
+    # name: (B, H, S, D, P, mask keep probability or None); the last round
+    # spread (lead and helper pieces), cut into half-tile pieces, or masked.
+    "last round spread, slices on tile bounds": (1, 1, 16384, 128, 2, None),
+    "whole rounds + spread last round": (1, 5, 20000, 128, 4, None),
+    "half tiles in pieces (Image share)": (1, 3, 4096, 128, 8, None),
+    "half tiles in pieces, D = 64, B = 2": (2, 1, 3000, 64, 4, None),
+    "block mask, B = 2": (2, 3, 1000, 128, 4, 0.4),
+}
+
+
+@pytest.mark.parametrize("case", sorted(WS_CASES))
+def test_slab_inputs_workspace_form_equals_unsharded(case):
+    """attn_fwd_slab_to_slab_ws_async equals attn_fwd_relayout_ws_async on
+    the unsharded tensors bit for bit (same schedule and merge, only the
+    load addressing differs), and meets the oracle on sampled rows."""
+    from gpu_util import sample_rows, slab_rows
+    B, H, S, D, P, keep_p = WS_CASES[case]
+    say(f"[slab-in ws] {case}: B={B} H={H} S={S} D={D} P={P} mask={keep_p}")
+    q, k, v = wl.random_qkv(B, H, S, D, seed=S + 11 * H)
+    words = None if keep_p is None else wl.pack_mask(wl.tile_mask_bool(H, S, keep_p, seed=S))
+    mask = None if words is None else mask_to_dev(words)
+    scale = 1.0 / math.sqrt(D)
+    g = Guarded((P, B, S // P, H, D))
+    fa.attn_fwd_slab_to_slab_ws_async(to_slabs(q, P), to_slabs(k, P), to_slabs(v, P), g.out,
+                                      B, H, S, D, P, scale, mask)
+    want = torch.empty((P, B, S // P, H, D), dtype=torch.bfloat16, device="cuda:0")
+    fa.attn_fwd_relayout_ws_async(to_dev(q), to_dev(k), to_dev(v), want, B, H, S, D, P, scale,
+                                  mask)
+    torch.cuda.synchronize()
+    g.check_guards()
+    assert g.unwritten() == 0
+    assert torch.equal(g.out.view(torch.int16), want.view(torch.int16))
+    rows = sample_rows(S, P, seed=S, n_random=8)
+    ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale,
+                           words, rows=rows)
+    assert_close(slab_rows(g.out, rows, S, P), ref, case)
