@@ -333,10 +333,11 @@ int run_relayout(const void* plain, void* out, int B, int H, int S, int D, int P
   return fa::launch_relayout(D, plain, out, rp, grid, stream) == 0 ? FA_OK : FA_ELAUNCH;
 }
 
-// Scratch of the allocation-free entry point: the dense tail round's partial
-// results, two slots per workgroup of a persistent grid of at most 256
-// (seg_floats(128) floats a slot), in a static device array so that the
-// entry point allocates nothing.  Each GPU the library runs on holds its own
+// Scratch of the allocation-free entry point: the partial results of a
+// dense call's spread last round, 512 slots of seg_floats(128) floats (a
+// round of t tiles spread over G workgroups uses t + G - 1 < 2 G slots, a
+// round cut into half-tile pieces at most G), in a static device array so
+// that the entry point allocates nothing.  Each GPU the library runs on holds its own
 // copy (68 MiB) until the process ends.  Host code never uses the array's
 // name as an address: scratch_address() takes the device address once per
 // device.
