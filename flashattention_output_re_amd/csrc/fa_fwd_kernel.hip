@@ -16,7 +16,7 @@
 // MFMA work in separate regions run by two wave groups in alternation (its
 // own header comment below has the schedule), in three forms: whole
 // 256-query tiles (dense), split-key 128-query half tiles (the last, partial
-// round of a dense launch) and split-key 128-query tiles over the kept tiles
+// round of a dense launch, whole or in pieces of their keys) and split-key 128-query tiles over the kept tiles
 // of one mask row (block-sparse).
 //
 // Layout choices (per wavefront, 32 queries):
@@ -558,9 +558,12 @@ __device__ __forceinline__ uint32_t clock_lo() { return (uint32_t)__builtin_amdg
 // hold the same queries and each computes on, and loads, its own K/V stream
 // with two buffers per tensor: in S(n), K stage n + 2 into the slot of K
 // stage n and V stage n + 1 into the slot of V stage n - 1 (both last read in
-// M(n - 1)), both first read in M(n + 1).  At the end the groups exchange
-// their partial (max, sum, O) through LDS; each merges and stores half of the
-// dims.
+// M(n - 1)), both first read in M(n + 1).  At the end group 1 hands its
+// partial (max, sum, O) to group 0 through LDS, and group 0 merges and stores
+// the half tile.  With a workspace (p.split_pieces > 1) a split unit is one
+// piece of a half tile's stages, split between the groups the same way, and
+// group 0 writes the merged piece to the workspace for fa_merge_split_kernel
+// instead of storing it.
 //
 // Masked units (MASKED = true, split-key) are the 128-query tiles of a block
 // mask: the row's K kept 128-key tiles give 2K stages in key order, group 0
