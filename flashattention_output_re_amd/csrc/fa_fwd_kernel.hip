@@ -16,8 +16,8 @@
 // MFMA work in separate regions run by two wave groups in alternation (its
 // own header comment below has the schedule), in three forms: whole
 // 256-query tiles (dense), split-key 128-query half tiles (the last, partial
-// round of a dense launch, whole or in pieces of their keys) and split-key 128-query tiles over the kept tiles
-// of one mask row (block-sparse).
+// round of a dense launch, whole or in pieces of their keys) and split-key
+// 128-query tiles over the kept tiles of one mask row (block-sparse).
 //
 // Layout choices (per wavefront, 32 queries):
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims of K from
