@@ -44,18 +44,22 @@ WORKLOAD_KEYS = {"video": "video-dit-share", "long": "long-video-share",
 
 # What one fused call launches on its stream (the roofline's "launch" is that
 # call: HIP events bracket it).  Dense, with a workspace: the kernel over
-# whole 256-query tiles, whose last, partial round is spread over every CU
-# (each tile's first stages on one workgroup, its remaining stages in slices
-# on the others), then the merge launch of that round's partial results.  Dense without a workspace: the kernel over whole tiles plus, when
-# the last round would fill at most half of the CUs, a second launch of its
-# split-key form for that round.  Masked: one launch of the split-key form
-# over 128-query tiles (one mask row each).
+# whole 256-query tiles, its last, partial round cut into key pieces -- at
+# least one full round before a last round at least half full: the full
+# rounds round-robin, the rest handed out from a counter, the last round's
+# tiles in pieces of falling length (a counter reset launch goes first);
+# otherwise the round spread over every CU, or run as split-key half tiles
+# cut into pieces -- then the merge launch of the pieces' partial results.
+# Dense without a workspace: the kernel over whole tiles plus, when the last
+# round would fill at most half of the CUs, a second launch of its split-key
+# form for that round.  Masked: one launch of the split-key form over
+# 128-query tiles (one mask row each).
 def kernel_label(D: int, dense: bool, tail_spread: bool = False) -> str:
     if dense and tail_spread:
-        return (f"fa_fwd_pp_kernel<{D}, Slab> (whole 256-query tiles; the last round's tiles "
-                "split at one stage, each tile's lead piece and slices of the tiles' remaining "
-                "stages spread over every CU) + fa_merge_kernel (the last round's partial "
-                "results)")
+        return (f"fa_fwd_pp_kernel<{D}, Slab> (whole 256-query tiles; the last round in key "
+                "pieces: handed out from a counter after full round-robin rounds, else spread "
+                "over every CU or as split-key half-tile pieces) + merge kernel (the pieces' "
+                "partial results)")
     if dense:
         return (f"fa_fwd_pp_kernel<{D}, Slab> (whole 256-query tiles; split-key half tiles "
                 "for a short last round)")

@@ -109,14 +109,21 @@ void div_magic(uint32_t d, uint32_t* magic, int* shift) {
 // tiles shared by the `cap` workgroups of the first launch -- tile i's
 // first tail_len stages on workgroup i, the tiles' remaining stages in
 // slices of tail_hlen on the others -- their partial results merged by a
-// second, small launch.
+// second, small launch -- or (dyn_pieces > 0, with a workspace) a dynamic
+// schedule: the first whole_units tiles, then the `tail` last tiles in
+// dyn_pieces key pieces of falling length, the full rounds of whole tiles
+// round-robin and everything after them handed to the workgroups of one
+// launch from a counter in the workspace as they free up, the pieces merged
+// by the second launch.
 struct DensePlan {
   int whole_units = 0, split_units = 0, cap = 0, split_cap = 0;
   int tail = 0, tail_len = 0, tail_hlen = 0;
+  int dyn_pieces = 0;
   int split_pieces = 0;    // > 1: each half tile cut into that many key pieces
   // Tiles of the split launch (two half tiles each, in split_pieces pieces).
   int tail_tiles() const { return split_units / (2 * (split_pieces > 1 ? split_pieces : 1)); }
   int64_t ws_bytes = 0;    // workspace the tail round needs
+  int64_t queue_offset = 0; // dynamic schedule: the counter's byte offset in it
 };
 
 // The shortest slice (in 64-key stages) for which the tail round is spread
@@ -129,12 +136,22 @@ constexpr int kTailMinSlice = 64;
 // The shortest piece (in 64-key stages, both groups together) a half tile
 // is cut into when the split launch is spread over a workspace.
 constexpr int kMinPieceStages = 16;
+// Dynamic schedule: the most key pieces per tail tile, the most partial
+// slots per workgroup of the grid, and the fewest 64-key stages of a tile it
+// cuts.  Workgroups run at unequal speeds (the chiplets of one device differ
+// by up to ~15% under load, by more on some devices), so a fixed partition
+// of the last round leaves the fast ones idle at the end; handing the last
+// round's tiles out in pieces of falling length as workgroups free up
+// evens out the finish.
+constexpr int kDynMaxPieces = 6;
+constexpr int kDynSlotsPerWorkgroup = 4;
+constexpr int kDynMinStages = 256;
 
 // Launch geometry of a call with params p (units = every tile): the number
 // of units per launch and the persistent grid caps, or FA_EDEVICE.
 // use_ws: the caller brings a workspace, so the tail round may be spread.
 int plan_call(int D, fa::StoreMode mode, bool masked, const fa::FwdParams& p, DensePlan* plan,
-              bool use_ws = false) {
+              bool use_ws = false, int64_t ws_limit = INT64_MAX) {
   const fa::Variant var = masked ? fa::Variant::Masked : fa::Variant::Whole;
   const int cap = grid_cap_for(D, mode, var);
   if (cap <= 0) return FA_EDEVICE;
@@ -148,6 +165,20 @@ int plan_call(int D, fa::StoreMode mode, bool masked, const fa::FwdParams& p, De
   // time of a whole tile), in a second launch on the same stream.
   const int tail = p.units % cap;
   const int stages = (p.S + 63) / 64;
+  // The dynamic schedule, for calls of at least one full round and a last
+  // round at least half full (t tail tiles in P = min(6, 4 cap / t) >= 4
+  // pieces each).  Workspace: one partial slot per piece, then the counter.
+  const int dyn_pieces = tail > 0 ? std::min(kDynMaxPieces, kDynSlotsPerWorkgroup * cap / tail) : 0;
+  const int64_t dyn_ws = (int64_t)tail * dyn_pieces * fa::seg_floats(D) * 4 + 256;
+  if (use_ws && p.units >= cap + tail && 2 * tail >= cap && stages >= kDynMinStages &&
+      dyn_ws <= ws_limit) {
+    plan->whole_units = p.units - tail;
+    plan->tail = tail;
+    plan->dyn_pieces = dyn_pieces;
+    plan->queue_offset = dyn_ws - 256;
+    plan->ws_bytes = dyn_ws;
+    return FA_OK;
+  }
   const int64_t span = (int64_t)tail * stages;
   const int64_t slice = (span + cap - 1) / cap;
   if (use_ws && tail > 0 && slice >= kTailMinSlice && slice < stages) {
@@ -232,6 +263,11 @@ int launch_call(int D, fa::StoreMode mode, const fa::FwdParams& p, const DensePl
     whole.tail = plan.tail;
     whole.tail_len = plan.tail_len;
     whole.tail_hlen = plan.tail_hlen;
+    if (plan.dyn_pieces > 0) {
+      whole.dyn_pieces = plan.dyn_pieces;
+      whole.queue = reinterpret_cast<int*>(reinterpret_cast<char*>(p.ws) + plan.queue_offset);
+      if (fa::launch_queue_reset(whole.queue, stream) != 0) return FA_ELAUNCH;
+    }
     if (fa::launch_fwd(D, mode, var, whole, plan.cap, stream, slab_in, 0) != 0) return FA_ELAUNCH;
     return fa::launch_merge(D, mode, whole, stream) == 0 ? FA_OK : FA_ELAUNCH;
   }
@@ -334,14 +370,15 @@ int run_relayout(const void* plain, void* out, int B, int H, int S, int D, int P
 }
 
 // Scratch of the allocation-free entry point: the partial results of a
-// dense call's spread last round, 512 slots of seg_floats(128) floats (a
-// round of t tiles spread over G workgroups uses t + G - 1 < 2 G slots, a
-// round cut into half-tile pieces at most G), in a static device array so
-// that the entry point allocates nothing.  Each GPU the library runs on holds its own
-// copy (68 MiB) until the process ends.  Host code never uses the array's
-// name as an address: scratch_address() takes the device address once per
-// device.
-constexpr size_t kScratchFloats = 2 * 256 * (size_t)fa::seg_floats(128);
+// dense call's last round, 1024 slots of seg_floats(128) floats (the dynamic
+// schedule's t < G tail tiles in P <= 4 G / t pieces use at most 4 G slots
+// and its counter 256 bytes after them; a round of t tiles spread over G
+// workgroups uses t + G - 1 < 2 G slots, a round cut into half-tile pieces
+// at most G), in a static device array so that the entry point allocates
+// nothing.  Each GPU the library runs on holds its own copy (136 MiB) until
+// the process ends.  Host code never uses the array's name as an address:
+// scratch_address() takes the device address once per device.
+constexpr size_t kScratchFloats = 4 * 256 * (size_t)fa::seg_floats(128) + 64;
 static __device__ __align__(256) float scratch[kScratchFloats];
 
 std::mutex g_scratch_mutex;
@@ -368,7 +405,10 @@ int run_noalloc(const void* q, const void* k, const void* v, void* out, int B, i
   int st = make_params(fa::StoreMode::Slab, q, k, v, out, B, H, S, D, P, scale, mask, false, &p);
   if (st != FA_OK) return st;
   DensePlan plan;
-  st = plan_call(D, fa::StoreMode::Slab, mask != nullptr, p, &plan, true);
+  // A plan within the scratch array: the dynamic schedule only where its
+  // partial slots fit, else the spread tail round (at most 2 cap - 1 slots).
+  st = plan_call(D, fa::StoreMode::Slab, mask != nullptr, p, &plan, true,
+                 (int64_t)sizeof(scratch));
   if (st != FA_OK) return st;
   if (plan.ws_bytes > (int64_t)sizeof(scratch)) return FA_ERANGE;
   if (plan.ws_bytes > 0) {

@@ -52,6 +52,17 @@ struct FwdParams {
   // unit_base * 2 + u / split_pieces; the pieces' partial results go to ws
   // slot u and fa_merge_split_kernel stores the half tiles.
   int split_pieces;
+  // Whole form only: a dynamic schedule when queue != nullptr -- items 0 ..
+  // units - 1 are whole units and items units + i the pieces of the `tail`
+  // tiles after them, each cut into P = dyn_pieces pieces, piece j holding
+  // the share (P - j) / (P (P + 1) / 2) of the key stages (piece i / tail of
+  // tile units + i % tail, partial result to ws slot (i % tail) P + i /
+  // tail); on a grid of G, workgroup slot s runs
+  // items s, s + G, ... below R = (units / G) G, then items R + q, q the old
+  // values of the counter *queue (zero at launch), one atomic add per item.
+  // fa_merge_kernel stores the tail tiles.
+  int* queue;
+  int dyn_pieces;
 };
 
 // Workspace slot of one tail segment, in floats: per wave (8) and lane (64)
@@ -76,6 +87,8 @@ int launch_merge(int D, StoreMode mode, const FwdParams& p, hipStream_t stream);
 // The merge of a split launch cut into pieces (p.split_pieces > 1, p.units
 // pieces, p.ws), on the stream after that launch; 0 on success.
 int launch_merge_split(int D, StoreMode mode, const FwdParams& p, hipStream_t stream);
+// Zeroes a dynamic schedule's counter, on the stream before its launch.
+int launch_queue_reset(int* queue, hipStream_t stream);
 // Resident workgroups per CU for the instance (D, mode, var); 0 on success.
 int kernel_occupancy(int D, StoreMode mode, Variant var, int* blocks_per_cu);
 

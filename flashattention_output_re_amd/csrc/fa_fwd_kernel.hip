@@ -641,6 +641,8 @@ void fa_fwd_pp_kernel(FwdParams p) {
   __shared__ float ml[SPLIT ? 2 * 256 : 1];
   // Masked launches: this workgroup's unit in each round of the schedule.
   __shared__ int plan_col[MASKED ? kPlanMaxRounds : 1];
+  // Dynamic schedule: the next item's counter value, from wave 0 to all.
+  __shared__ int dyn_next_lds;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -762,7 +764,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
   // piece of tile i slot t + i + hh (distinct, as the helpers' tiles never
   // go back; below t + G - 1).
   auto tail_segments = [&](int sid) FA_INL {
-    if (SPLIT || MASKED || p.tail <= 0) return 0;
+    if (SPLIT || MASKED || p.tail <= 0 || p.queue) return 0;
     if (sid < p.tail) return 1;
     const int e = ns - p.tail_len;
     if (e <= 0) return 0;
@@ -1170,14 +1172,46 @@ void fa_fwd_pp_kernel(FwdParams p) {
       n_units = rounds - (plan_col[rounds - 1] < 0 ? 1 : 0);
     }
   }
-  const int n_items = n_units + tail_segments(slot);
+  // Dynamic schedule (whole form, p.queue set): the item index is the
+  // position in the launch's item list (whole units, then the tail tiles'
+  // pieces, piece by piece); the full rounds of whole units run round-robin
+  // (item slot + i G, so that the 32 workgroups of a chiplet start their
+  // tiles together and share each K/V stage in its L2), every later item
+  // is dyn_static + the queue counter's old value, fetched early in the
+  // Q-loop by lane 0 of wave 0 (one atomic add per item; it retires with
+  // the stage DMA waits that follow it) and passed to the other waves
+  // through LDS at the barrier that ends the Q-loop.
+  const bool dyn = !SPLIT && !MASKED && INSTR == 0 && p.queue != nullptr;
+  const int dyn_n = dyn ? p.units + p.tail * p.dyn_pieces : 0;
+  const int dyn_static = dyn ? p.units / G * G : 0;
+  auto make_dyn = [&](int i) FA_INL {
+    if (i < p.units) return make_unit(i);
+    Unit u;
+    const int pi = i - p.units, j = pi / p.tail, ti = pi - j * p.tail;
+    make_tile(p.units + ti, u);
+    u.uidx = -1;
+    u.qrow = u.qt * 256 + wave * 32 + l32;
+    // Piece j of P holds the share (P - j) / (P (P + 1) / 2) of the keys:
+    // the pieces handed out last are the shortest, so that the workgroups
+    // finish close together.
+    const int P = p.dyn_pieces, tot = P * (P + 1) / 2;
+    const int c0 = j * P - j * (j - 1) / 2, c1 = c0 + P - j;
+    u.s0 = ns * c0 / tot;
+    u.nst = ns * c1 / tot - u.s0;
+    u.nloop = u.nst;
+    u.seg = ti * p.dyn_pieces + j;
+    return u;
+  };
+  const int n_items = dyn ? (slot < dyn_n ? 1 : 0) : n_units + tail_segments(slot);
   auto make_item = [&](int i) FA_INL {
+    if (dyn) return make_dyn(i);
     if (planned) return make_unit(__builtin_amdgcn_readfirstlane(plan_col[i]));
     return i < n_units ? make_unit(slot + i * G) : make_segment(slot, i - n_units);
   };
   if (n_items == 0) return;
-  int item = 0;
-  cur = make_item(0);
+  int item = dyn ? slot : 0;
+  int dyn_got = 0;
+  cur = make_item(item);
   start_stream(cur);
   prologue(cur);
   wait_vm<0>();
@@ -1188,6 +1222,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
     barrier_keep_dma();
     const uint32_t t_start = INSTR ? clock_lo() : 0u;
     qk_mfma<D>(s, kbuf(0), qf, l32, g);
+    if (dyn && item + G >= dyn_static && wave == 0 && lane == 0) dyn_got = atomicAdd(p.queue, 1);
     // Every read of K stage 0 has returned before the barrier (split units
     // refill its slot in S(0)).
     wait_lds();
@@ -1208,7 +1243,12 @@ void fa_fwd_pp_kernel(FwdParams p) {
     wait_dma();   // DMA of stages past the end, before the buffers are reused
     const uint32_t t_epi = INSTR ? clock_lo() : 0u;
     // Group 0's trailing region ends with the barrier that ends group 1's
-    // last M: every wave's reads of the K/V buffers are over.
+    // last M: every wave's reads of the K/V buffers are over.  Dynamic
+    // schedule: wave 0 posts the next item's counter value before it.
+    if (dyn && wave == 0) {
+      if (lane == 0) dyn_next_lds = dyn_got;
+      wait_lds();
+    }
     if (grp == 0) barrier_keep_dma();
 
     // Split units: group 1 hands its partial state over through stream 0's
@@ -1251,11 +1291,15 @@ void fa_fwd_pp_kernel(FwdParams p) {
 
     // The tile boundary: the next unit's prologue, then this unit's stores
     // (COUPLED: the stores, their completion, then the prologue).
-    const bool more = item + 1 < n_items;
+    const int next_item = !dyn ? item + 1
+                          : item + G < dyn_static
+                              ? item + G
+                              : dyn_static + __builtin_amdgcn_readfirstlane(dyn_next_lds);
+    const bool more = dyn ? next_item < dyn_n : next_item < n_items;
     Unit nxt = cur;
     auto next_prologue = [&]() FA_INL {
       if (more) {
-        nxt = make_item(item + 1);
+        nxt = make_item(next_item);
         start_stream(nxt);
         prologue(nxt);
       }
@@ -1325,7 +1369,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
     if constexpr (INSTR) t_ready = clock_lo();
     if (!more) break;
     cur = nxt;
-    ++item;
+    item = next_item;
   }
 }
 
@@ -1396,10 +1440,15 @@ __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
   const int tile = p.units + ti;
   const int bh = tile / p.nqt, qt = tile - bh * p.nqt;
   const int b = bh / p.H, h = bh - b * p.H;
+  // Dynamic schedule: the tile's dyn_pieces pieces, slots ti * pieces + k.
+  // Otherwise its lead and the helpers that met its end.
+  const bool dyn = p.queue != nullptr;
   const int e = ns - p.tail_len, Lh = p.tail_hlen;
-  const int h0 = e > 0 ? ti * e / Lh : 0;
-  const int np = e > 0 ? ((ti + 1) * e - 1) / Lh - h0 + 2 : 1;   // lead + helpers
-  auto slot = [&](int k) { return k == 0 ? ti : p.tail + ti + h0 + k - 1; };
+  const int h0 = !dyn && e > 0 ? ti * e / Lh : 0;
+  const int np = dyn ? p.dyn_pieces : e > 0 ? ((ti + 1) * e - 1) / Lh - h0 + 2 : 1;
+  auto slot = [&](int k) {
+    return dyn ? ti * p.dyn_pieces + k : k == 0 ? ti : p.tail + ti + h0 + k - 1;
+  };
   f32x16 acc[NDB];
   float l;
   merge_partials<D>(p.ws, np, slot, wave, lane, acc, l);
@@ -1431,6 +1480,14 @@ __global__ __launch_bounds__(64) void fa_merge_split_kernel(FwdParams p) {
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   store_rows<D, MODE, NDB>(p, acc, inv, qt * 256 + (hf & 1) * 128 + wave * 32 + l32, 0, b, h, bh,
                            g, lane);
+}
+
+__global__ void fa_queue_reset_kernel(int* queue) { *queue = 0; }
+
+int launch_queue_reset(int* queue, hipStream_t stream) {
+  if (!queue) return -1;
+  hipLaunchKernelGGL(fa_queue_reset_kernel, dim3(1), dim3(1), 0, stream, queue);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // Kernel form of each variant: split-key units, masked units.

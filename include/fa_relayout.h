@@ -141,7 +141,17 @@ int relayout_to_slabs(const void* plain, void* out_slabs, int B, int H, int S, i
 /* The dense calls above run the last, partial round of whole 256-query tiles
  * (when fewer tiles remain than the GPU has resident workgroups) as half
  * tiles inside each workgroup, which needs no memory beyond the caller's
- * tensors.  The _ws_ forms instead spread that round over every workgroup:
+ * tensors.  The _ws_ forms instead share that round among the workgroups.
+ * A call of at least one full round whose last round holds t >= G/2 tiles
+ * of at least 256 key stages runs a dynamic schedule: the full rounds
+ * round-robin, then every later tile -- and the last t tiles cut into P =
+ * min(6, 4 G / t) key pieces of falling length (piece j of P holding the
+ * share (P - j) / (P (P + 1) / 2) of the keys), all first pieces before any
+ * second -- handed to the workgroups one at a time, from a counter in the
+ * workspace (zeroed by a launch of the call itself), as they free up: the
+ * workgroups of one GPU do not all run at one speed, and the pieces let the
+ * faster ones take more of the end.  Otherwise the round is spread over
+ * every workgroup:
  * each of its t tiles is split at the same key stage L (about t/G of the
  * tile for G workgroups); workgroup i runs tile i's first L stages -- the t
  * leads start together and stream each tile's K/V in step, as full rounds
@@ -190,16 +200,20 @@ int attn_fwd_slab_to_slab_ws_async(const void* q_slabs, const void* k_slabs, con
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation: the call of
  * attn_fwd_relayout_ws_async with the library's own workspace, a static
- * device array of 68 MiB that every GPU the library runs on holds until the
+ * device array of 136 MiB that every GPU the library runs on holds until the
  * process ends, so a call needs no memory beyond q, k, v, out_slabs (and the
  * mask).  Same arguments (no workspace), status codes and result as
  * attn_fwd_relayout_ws_async; FA_ERANGE when a call would need more than the
- * array holds (only on GPUs with more than 256 resident workgroups),
+ * array holds (only on GPUs with more than 512 resident workgroups; above
+ * 256, where the dynamic schedule's pieces may not fit, a call whose pieces
+ * do not runs the spread round instead, equal within rounding),
  * FA_EDEVICE when the array's device address cannot be obtained.  Every call
  * on one GPU shares that GPU's array: calls that may overlap on one GPU
  * (concurrent streams) race and must not be made; calls ordered on one
  * stream are safe.  Nothing carries over between calls (each call writes
- * every workspace slot it reads), so nothing needs clearing. */
+ * every workspace slot it reads, and zeroes the dynamic schedule's counter
+ * with a launch of its own before the kernel that counts), so nothing needs
+ * clearing. */
 int attn_fwd_relayout_noalloc_async(const void* q, const void* k, const void* v, void* out_slabs,
                                     int B, int H, int S, int D, int P, float scale,
                                     const uint64_t* mask, void* stream);

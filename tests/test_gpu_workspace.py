@@ -57,15 +57,20 @@ def run_plain_ws(q, k, v, scale, mask=None):
     return g.out
 
 
-# (B, H, S, D, P) from the CU count n (slice lengths for 256 CUs).  The tail
-# round is spread as whole-tile pieces when a slice holds at least 64 stages;
-# shorter tails run as half tiles, cut into key pieces of at least 16 stages
-# when that leaves workgroups idle.
+# (B, H, S, D, P) from the CU count n (slice lengths for 256 CUs).  Calls of
+# at least one full round and a last round at least half full, of tiles of at
+# least 256 key stages, run the dynamic schedule (the last round's t tiles in
+# min(6, 4 n / t) key pieces of falling length, handed out from a counter);
+# other tail rounds are spread as whole-tile pieces when a slice holds at
+# least 64 stages; shorter tails run as half tiles, cut into key pieces of at
+# least 16 stages when that leaves workgroups idle.
 SHAPES = {
     "all tail, slices on tile bounds": lambda n: (1, 1, 16384, 128, 2),        # L = 64
     "all tail, unaligned slices, ragged S": lambda n: (1, 1, 20000, 128, 8),   # L = 97
-    "whole round + tail, unaligned": lambda n: (1, 5, 20000, 128, 4),          # L = 170
+    "whole round + tail, unaligned": lambda n: (1, 4, 20000, 128, 4),          # L = 74
     "all tail, D=64, B=2": lambda n: (2, 1, 20000, 64, 4),                     # L = 194
+    "dynamic, ragged S": lambda n: (1, 5 * n // 256, 20000, 128, 4),           # t = 139
+    "dynamic, D=64, B=2": lambda n: (2, 3 * n // 256, 16400, 64, 4),           # t = 134
     "half tiles in 2 pieces (Image share)": lambda n: (1, 3, 4096, 128, 8),
     "half tiles in 4 pieces": lambda n: (1, 1, 4096, 128, 2),
     "half tiles in 2 pieces, D=64, B=2, ragged S": lambda n: (2, 1, 3000, 64, 4),
@@ -128,8 +133,8 @@ def test_ws_full_size_sampled(name):
 
 
 def test_ws_every_row_of_a_tail_tile():
-    """Every row of the Video share's last head, whose 128 tiles all run in
-    the tail round (spread over every workgroup and merged), against the
+    """Every row of the Video share's last head, whose 128 tiles all run as
+    key pieces (spread over the workgroups and merged), against the
     oracle."""
     w = wl.WORKLOADS["video"]
     inp = wl.make("video")
@@ -198,11 +203,13 @@ def test_ws_rejects_small_or_misaligned_workspace():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_ws_graph_capture_replays():
-    """A _ws_ call (two launches) recorded in a HIP graph with a
-    preallocated workspace replays bit-identically to the eager call, with
-    eager work between replays."""
-    B, H, S, D, P = 1, 1, 16384, 128, 2
+@pytest.mark.parametrize("shape", [(1, 1, 16384, 128, 2), (1, 5, 20000, 128, 4)],
+                         ids=["spread tail", "dynamic"])
+def test_ws_graph_capture_replays(shape):
+    """A _ws_ call (two launches; the dynamic schedule's counter reset makes
+    three) recorded in a HIP graph with a preallocated workspace replays
+    bit-identically to the eager call, with eager work between replays."""
+    B, H, S, D, P = shape
     q, k, v = (to_dev(t) for t in wl.random_qkv(B, H, S, D, seed=7))
     ws = torch.empty(binding.attn_fwd_workspace_bytes(B, H, S, D), dtype=torch.uint8,
                      device=q.device)
