@@ -1071,13 +1071,15 @@ void fa_fwd_pp_kernel(FwdParams p) {
   };
 
   // This workgroup's work items: the launch's units slot, slot + G, ... and
-  // then (whole form) its tail segments.  Dense units in XCD-aware order.
-  // Masked units run on the schedule below (plain order beyond its limits):
-  // on a 30%-dense block mask the XCD-aware order measured slower (its
-  // workgroups skip different tiles, so they do not stream K/V in step as
-  // dense tiles do).
+  // then (whole form) its tail segments, slots in XCD-aware order.  Masked
+  // units run on the schedule below (plain order beyond its limits), which
+  // deals each round's units by kept-tile count to consecutive slots: an
+  // XCD's workgroups then hold units of about the same count, which walk
+  // their rows' kept tiles at about the same pace, so the tiles that several
+  // of them keep meet in its L2 close together in time (1.6% faster on a
+  // 30%-dense mask than slots dealt round-robin over the XCDs).
   const int G = (int)gridDim.x;
-  const int slot = MASKED ? (int)blockIdx.x : xcd_slot(blockIdx.x, G);
+  const int slot = xcd_slot(blockIdx.x, G);
   int n_units = slot < p.units ? (p.units - slot + G - 1) / G : 0;
   // Masked schedule.  A masked unit's Q-loop time is close to linear in K,
   // its row's kept tiles, so the plain order -- G units per round -- leaves
@@ -1177,10 +1179,11 @@ void fa_fwd_pp_kernel(FwdParams p) {
   // pieces, piece by piece); the full rounds of whole units run round-robin
   // (item slot + i G, so that the 32 workgroups of a chiplet start their
   // tiles together and share each K/V stage in its L2), every later item
-  // is dyn_static + the queue counter's old value, fetched early in the
-  // Q-loop by lane 0 of wave 0 (one atomic add per item; it retires with
-  // the stage DMA waits that follow it) and passed to the other waves
-  // through LDS at the barrier that ends the Q-loop.
+  // is dyn_static + the queue counter's old value, fetched by lane 0 of
+  // wave 0 once the item's last stage is in (one atomic add per item, its
+  // return awaited with no DMA left in flight; fetched earlier, the value
+  // would hold a register through the stage loop) and passed to the other
+  // waves through LDS at the barrier that ends the Q-loop.
   const bool dyn = !SPLIT && !MASKED && INSTR == 0 && p.queue != nullptr;
   const int dyn_n = dyn ? p.units + p.tail * p.dyn_pieces : 0;
   const int dyn_static = dyn ? p.units / G * G : 0;
@@ -1210,7 +1213,6 @@ void fa_fwd_pp_kernel(FwdParams p) {
   };
   if (n_items == 0) return;
   int item = dyn ? slot : 0;
-  int dyn_got = 0;
   cur = make_item(item);
   start_stream(cur);
   prologue(cur);
@@ -1222,7 +1224,6 @@ void fa_fwd_pp_kernel(FwdParams p) {
     barrier_keep_dma();
     const uint32_t t_start = INSTR ? clock_lo() : 0u;
     qk_mfma<D>(s, kbuf(0), qf, l32, g);
-    if (dyn && item + G >= dyn_static && wave == 0 && lane == 0) dyn_got = atomicAdd(p.queue, 1);
     // Every read of K stage 0 has returned before the barrier (split units
     // refill its slot in S(0)).
     wait_lds();
@@ -1244,9 +1245,10 @@ void fa_fwd_pp_kernel(FwdParams p) {
     const uint32_t t_epi = INSTR ? clock_lo() : 0u;
     // Group 0's trailing region ends with the barrier that ends group 1's
     // last M: every wave's reads of the K/V buffers are over.  Dynamic
-    // schedule: wave 0 posts the next item's counter value before it.
+    // schedule: wave 0 fetches the next item's counter value and posts it
+    // before that barrier.
     if (dyn && wave == 0) {
-      if (lane == 0) dyn_next_lds = dyn_got;
+      if (lane == 0 && item + G >= dyn_static) dyn_next_lds = atomicAdd(p.queue, 1);
       wait_lds();
     }
     if (grp == 0) barrier_keep_dma();

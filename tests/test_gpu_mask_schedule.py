@@ -2,13 +2,16 @@
 
 Every workgroup derives the same schedule from the mask: the rounds of G
 units of the plain order (G = the persistent grid), each dealt in decreasing
-kept-tile count K (ties by index) in snake order -- in even rounds workgroup
-w takes the w-th costliest unit, in odd rounds the (G - 1 - w)-th.  The
-timestamped instances record which workgroup ran each unit
-(include/fa_instrument.h), so the test compares that assignment with the
-schedule computed here from its definition; beyond the schedule's limits
-(more mask rows than kb0 holds as int counts, 8192 at D = 128, or more than
-256 rounds) the launch keeps the plain order, unit u on workgroup u mod G.
+kept-tile count K (ties by index) in snake order -- in even rounds slot w
+takes the w-th costliest unit, in odd rounds the (G - 1 - w)-th, where the
+workgroup with block id b holds slot (b mod 8) G/8 + floor(b / 8) when 8
+divides G (the XCD-aware order: the hardware deals blocks to the 8 XCDs
+round-robin), else slot b.  The timestamped instances record which
+workgroup ran each unit (include/fa_instrument.h), so the test compares that
+assignment with the schedule computed here from its definition; beyond the
+schedule's limits (more mask rows than kb0 holds as int counts, 8192 at D =
+128, or more than 256 rounds) the launch keeps the plain order, unit u on
+slot u mod G.
 The outputs equal the product kernel's bit for bit and meet the float64
 oracle on sampled rows.
 """
@@ -32,8 +35,13 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
+def slot_of_block(b, G):
+    """The XCD-aware slot of block id b on a grid of G."""
+    return (b % 8) * (G // 8) + b // 8 if G % 8 == 0 else b
+
+
 def expected_schedule(kept, G):
-    """Workgroup of each unit under the round-wise snake rule."""
+    """Slot of each unit under the round-wise snake rule."""
     units = len(kept)
     wg_of = np.full(units, -1, dtype=np.int64)
     for r, base in enumerate(range(0, units, G)):
@@ -91,8 +99,8 @@ def test_masked_schedule(case):
     units = B * H * nT
     assert list(launch) == [units, 0]
     (rec,) = tile_stamps.records(stamps.cpu().numpy().view(np.uint32), launch)
-    ran_on = rec[:, 0, 6].astype(np.int64)
     G = min(units, _cus())
+    ran_on = slot_of_block(rec[:, 0, 6].astype(np.int64), G)
     kept = np.tile(keepm.sum(-1).reshape(-1), B).astype(np.int64)
     if H * nT > 8192 or (units + G - 1) // G > 256:
         want = np.arange(units) % G
