@@ -638,7 +638,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t vb2[NBUF == 4 ? NG : 1][NBUF == 4 ? E : 8];
   __shared__ __attribute__((aligned(16))) uint16_t vb3[NBUF == 4 ? NG : 1][NBUF == 4 ? E : 8];
   // Group 1's running (max, sum) hand-over (split units only).
-  __shared__ float ml[SPLIT ? 2 * 256 : 1];
+  __shared__ float ml[SPLIT ? 4 * 256 : 1];
   // Masked launches: this workgroup's unit in each round of the schedule.
   __shared__ int plan_col[MASKED ? kPlanMaxRounds : 1];
   // Dynamic schedule: the next item's counter value, from wave 0 to all.
@@ -882,15 +882,18 @@ void fa_fwd_pp_kernel(FwdParams p) {
   f32x16 acc[NDB];          // O^T accumulator
   float m_run = 0.0f, l_run = 0.0f;
 
-  // Prologue of unit u: the Q fragments and the first K/V stages of this
-  // wave's stream -- K stages 0 and 1 and V stage 0 (SPLIT: each group, its
-  // own stream) or K stages 0-2 (group 0) and V stages 0-2 (group 1).
-  auto prologue = [&](const Unit& u) FA_INL {
+  // Prologue of unit u: the Q fragments (prologue_q) and the first K/V
+  // stages of this wave's stream (prologue_kv) -- K stages 0 and 1 and V
+  // stage 0 (SPLIT: each group, its own stream) or K stages 0-2 (group 0)
+  // and V stages 0-2 (group 1).
+  auto prologue_q = [&](const Unit& u) FA_INL {
     const uint32_t qbase = !SLAB_IN ? (uint32_t)(u.qrow * D * 2)
                            : u.qrow < p.S ? slab_row(u, (uint32_t)u.qrow) : in_bytes;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, load16(u.rq, qbase + ks * 32 + g * 16));
+  };
+  auto prologue_kv = [&](const Unit& u) FA_INL {
     if (SPLIT || grp == 0) {
       dma_k(u, 0, stage_key(u, 0));
       dma_k(u, 1, stage_key(u, 1));
@@ -1215,7 +1218,8 @@ void fa_fwd_pp_kernel(FwdParams p) {
   int item = dyn ? slot : 0;
   cur = make_item(item);
   start_stream(cur);
-  prologue(cur);
+  prologue_q(cur);
+  prologue_kv(cur);
   wait_vm<0>();
   uint32_t t_ready = INSTR ? clock_lo() : 0u;
   for (;;) {
@@ -1253,57 +1257,94 @@ void fa_fwd_pp_kernel(FwdParams p) {
     }
     if (grp == 0) barrier_keep_dma();
 
-    // Split units: group 1 hands its partial state over through stream 0's
-    // four K/V buffers, idle by now: wave wq's O^T accumulator (NDB x 16
-    // floats per lane, one buffer exactly) at float (db * 16 + r) * 64 + lane
-    // of buffer wq, its running max and sum in ml; group 0 merges and stores.
-    if constexpr (SPLIT) {
-      static_assert(NDB * 16 * 64 * 4 == E * 2, "one buffer per wave");
-      float* const area = reinterpret_cast<float*>(wq == 0 ? kb0[0] : wq == 1 ? kb1[0]
-                                                   : wq == 2 ? vb0[0] : vb1[0]);
-      if (grp == 1) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) area[(db * 16 + r) * 64 + lane] = acc[db][r];
-        ml[wq * 64 + lane] = m_run;
-        ml[256 + wq * 64 + lane] = l_run;
-      }
-      __syncthreads();
-      if (grp == 0) {
-        const float m_y = ml[wq * 64 + lane];
-        const float l_y = ml[256 + wq * 64 + lane];
-        const float m = fmaxf(m_run, m_y);
-        const float ax = __builtin_amdgcn_exp2f(m_run - m);
-        const float ay = __builtin_amdgcn_exp2f(m_y - m);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc[db][r] = acc[db][r] * ax + area[(db * 16 + r) * 64 + lane] * ay;
-        l_run = l_run * ax + l_y * ay;
-        m_run = m;
-      }
-      // Group 0 has read the hand-over area before the next unit's prologue
-      // refills stream 0's buffers.
-      __syncthreads();
-    }
-    const float l_tot = halves_sum(l_run);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-
-    // The tile boundary: the next unit's prologue, then this unit's stores
-    // (COUPLED: the stores, their completion, then the prologue).
+    // The next item, and its Q fragments: the registers are free once the
+    // last stage's scores are formed, and the loads, issued ahead of the
+    // epilogue's merge and normalisation, leave the vector memory path to
+    // the K/V DMA at the boundary (the CU issues the next unit's ~160 KiB of
+    // loads and this unit's stores through one path, and the next Q-loop
+    // starts only when they are in).  COUPLED and LATE keep all of the
+    // prologue after the stores.
     const int next_item = !dyn ? item + 1
                           : item + G < dyn_static
                               ? item + G
                               : dyn_static + __builtin_amdgcn_readfirstlane(dyn_next_lds);
     const bool more = dyn ? next_item < dyn_n : next_item < n_items;
+    constexpr bool kEarlyQ = !COUPLED && !LATE;
     Unit nxt = cur;
+    if (kEarlyQ && more) {
+      nxt = make_item(next_item);
+      prologue_q(nxt);
+    }
+
+    // Split units: the two groups hold the same queries over different keys
+    // and exchange half of their state through stream 0's four K/V buffers,
+    // idle by now: wave wq of group 1 hands over its O^T accumulator's dims
+    // [0, D/2), wave wq of group 0 its dims [D/2, D) (NDB/2 x 16 floats per
+    // lane each, at float (db * 16 + r) * 64 + lane of buffer wq, the halves
+    // disjoint), both their running max and sum (ml, by group); then each
+    // merges the half it kept -- with x group 0's state and y group 1's,
+    // O = O_x 2^(m_x - m) + O_y 2^(m_y - m), m = max(m_x, m_y), l alike --
+    // and stores it (group 0 dims [0, D/2), group 1 dims [D/2, D)).
+    constexpr int H2 = NDB / 2;
+    if constexpr (SPLIT) {
+      static_assert(NDB * 16 * 64 * 4 == E * 2, "one buffer per wave");
+      float* const area = reinterpret_cast<float*>(wq == 0 ? kb0[0] : wq == 1 ? kb1[0]
+                                                   : wq == 2 ? vb0[0] : vb1[0]);
+      auto hand_over = [&](auto OFF) FA_INL {
+        constexpr int off = decltype(OFF)::value;
+#pragma unroll
+        for (int db = off; db < off + H2; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) area[(db * 16 + r) * 64 + lane] = acc[db][r];
+      };
+      if (grp == 0)
+        hand_over(std::integral_constant<int, H2>{});
+      else
+        hand_over(std::integral_constant<int, 0>{});
+      ml[grp * 512 + wq * 64 + lane] = m_run;
+      ml[grp * 512 + 256 + wq * 64 + lane] = l_run;
+      __syncthreads();
+      const float m_o = ml[(1 - grp) * 512 + wq * 64 + lane];
+      const float l_o = ml[(1 - grp) * 512 + 256 + wq * 64 + lane];
+      const float m_x = grp == 0 ? m_run : m_o, m_y = grp == 0 ? m_o : m_run;
+      const float l_x = grp == 0 ? l_run : l_o, l_y = grp == 0 ? l_o : l_run;
+      const float m = fmaxf(m_x, m_y);
+      const float ax = __builtin_amdgcn_exp2f(m_x - m);
+      const float ay = __builtin_amdgcn_exp2f(m_y - m);
+      auto merge_kept = [&](auto OFF) FA_INL {
+        constexpr int off = decltype(OFF)::value;
+#pragma unroll
+        for (int db = off; db < off + H2; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float other = area[(db * 16 + r) * 64 + lane];
+            acc[db][r] = off == 0 ? acc[db][r] * ax + other * ay : other * ax + acc[db][r] * ay;
+          }
+      };
+      if (grp == 0)
+        merge_kept(std::integral_constant<int, 0>{});
+      else
+        merge_kept(std::integral_constant<int, H2>{});
+      l_run = l_x * ax + l_y * ay;
+      m_run = m;
+      // Both groups have read the hand-over area before the next unit's
+      // prologue refills stream 0's buffers.
+      __syncthreads();
+    }
+    const float l_tot = halves_sum(l_run);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+
+    // The tile boundary: the rest of the next unit's prologue, then this
+    // unit's stores (COUPLED: the stores, their completion, then the
+    // prologue).
     auto next_prologue = [&]() FA_INL {
       if (more) {
-        nxt = make_item(next_item);
+        if (!kEarlyQ) {
+          nxt = make_item(next_item);
+          prologue_q(nxt);
+        }
         start_stream(nxt);
-        prologue(nxt);
+        prologue_kv(nxt);
       }
     };
     if (!COUPLED && !LATE) next_prologue();
@@ -1341,28 +1382,48 @@ void fa_fwd_pp_kernel(FwdParams p) {
       else
         wait_vm<nst>();
     };
-    // Whole units: every wave stores its 32 queries.  Split units: group 0
-    // stores the merged tile, group 1 nothing.  Tail segments and the pieces
-    // of a split launch cut into pieces: every storing wave (all eight, or
-    // group 0 after the groups' merge) writes its partial result -- the O^T
-    // accumulator normalised by its own row sum (the same products
-    // store_rows forms, so the accumulator is not kept twice), its running
-    // max and that row sum -- to workspace slot cur.seg for the merge kernel
-    // (layout: seg_floats, wave w's part at w).
-    if (SPLIT && grp == 1) {
-      finish(std::integral_constant<int, 0>{});
-    } else if (!MASKED && cur.seg >= 0) {
+    // Whole units: every wave stores its 32 queries.  Split units: each
+    // group its half of the dims of the merged tile.  Tail segments and the
+    // pieces of a split launch cut into pieces: every storing wave writes
+    // its partial result -- the O^T accumulator normalised by its own row sum
+    // (the same products store_rows forms, so the accumulator is not kept
+    // twice), its running max and that row sum -- to workspace slot cur.seg
+    // for the merge kernel (layout: seg_floats, wave w's part at w; split
+    // units: the group-0 wave wq's part, its dims from both groups, max and
+    // sum from group 0).
+    auto write_partial = [&](auto OFF, auto N, int w) FA_INL {
+      constexpr int off = decltype(OFF)::value, n = decltype(N)::value;
       float* const ws = p.ws + (size_t)cur.seg * seg_floats(D);
       typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = off; db < off + n; ++db)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          *reinterpret_cast<f32x4*>(ws + ((wave * 4 * NDB + db * 4 + rr) * 64 + lane) * 4) =
+          *reinterpret_cast<f32x4*>(ws + ((w * 4 * NDB + db * 4 + rr) * 64 + lane) * 4) =
               f32x4{acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv, acc[db][4 * rr + 2] * inv,
                     acc[db][4 * rr + 3] * inv};
-      *reinterpret_cast<f32x4*>(ws + seg_ml_offset(D) + (wave * 64 + lane) * 4) =
-          f32x4{m_run, l_tot, 0.0f, 0.0f};
+      if (off == 0)
+        *reinterpret_cast<f32x4*>(ws + seg_ml_offset(D) + (w * 64 + lane) * 4) =
+            f32x4{m_run, l_tot, 0.0f, 0.0f};
+    };
+    if constexpr (SPLIT) {
+      auto store_half = [&](auto OFF) FA_INL {
+        constexpr int off = decltype(OFF)::value;
+        if (!MASKED && cur.seg >= 0) {
+          write_partial(OFF, std::integral_constant<int, H2>{}, wq);
+          finish(std::integral_constant<int, 4 * H2 + (off == 0 ? 1 : 0)>{});
+        } else {
+          const f32x16(&o)[H2] = *reinterpret_cast<const f32x16(*)[H2]>(&acc[off]);
+          store_rows<D, MODE, H2>(p, o, inv, cur.qrow, 32 * off, cur.b, cur.h, cur.bh, g, lane);
+          finish(std::integral_constant<int, 2 * H2>{});
+        }
+      };
+      if (grp == 0)
+        store_half(std::integral_constant<int, 0>{});
+      else
+        store_half(std::integral_constant<int, H2>{});
+    } else if (cur.seg >= 0) {
+      write_partial(std::integral_constant<int, 0>{}, std::integral_constant<int, NDB>{}, wave);
       finish(std::integral_constant<int, 4 * NDB + 1>{});
     } else {
       store_rows<D, MODE, NDB>(p, acc, inv, cur.qrow, 0, cur.b, cur.h, cur.bh, g, lane);
