@@ -336,7 +336,8 @@ def write_profile_report(workload: str, d: str):
     fwd = [n for n in stats if "fa_fwd" in n]
     fused = sorted([n for n in fwd if "(fa::StoreMode)0" in n and product(n)
                     and flags(n)[3] == "false"] +
-                   [n for n in stats if "fa_merge" in n and "(fa::StoreMode)0" in n])
+                   [n for n in stats if "fa_merge" in n and "(fa::StoreMode)0" in n] +
+                   [n for n in stats if "fa_queue_reset" in n])
     slab_in = sorted(n for n in fwd if product(n) and flags(n)[3] == "true")
     avg_s = {n: float(stats[n]["AverageNs"]) * 1e-9 for n in fused}
     call_s = sum(avg_s.values())
@@ -370,8 +371,11 @@ def write_profile_report(workload: str, d: str):
           "units, slab-layout inputs, timestamped instance (false, false for the middle two: whole "
           "256-query tiles; true, false: split-key half tiles of a short last round, a second launch "
           "on the same stream; true, true: masked 128-query tiles). `fa_merge_kernel`: the merge "
-          "of a dense call's last round, spread over every CU as stage slices (the workspace "
-          "entry points). `relayout_kernel<16>`: the serial baseline's standalone copy.\n",
+          "of a dense call's last-round key pieces (the workspace entry points: pieces handed out "
+          "from a counter, or stage slices spread over every CU); `fa_merge_split_kernel`: the "
+          "merge of split half tiles cut into key pieces; `fa_queue_reset_kernel`: the one-thread "
+          "launch that zeroes the dynamic schedule's counter. `relayout_kernel<16>`: the serial "
+          "baseline's standalone copy.\n",
           summary("trace", f"trace_{workload}"),
           f"One fused call = {' + '.join(f'{avg_s[n] * 1e3:.4f}' for n in fused)} = {call_s * 1e3:.4f} ms "
           f"under the tracer; {flop:.4g} algorithmic FLOP per call -> {flop / call_s / 1e12:.1f} TFLOP/s "

@@ -197,8 +197,9 @@ def summarize(docs: list, command: str) -> str:
          "record the low 32 bits of `s_memtime` per unit and wave; spans below are differences "
          "within one workgroup, in shader cycles, over every pair of consecutive units a "
          "workgroup runs (p50 / p90 over units x 8 waves).  Boundary forms: **piggyback** (the "
-         "product kernel's: next unit's Q loads and first K/V stages, then the tile's stores, "
-         "wait for the loads only), **ordered** (the stores, then the next unit's loads, one wait "
+         "product kernel's: next unit's Q loads -- issued before the epilogue's merge and "
+         "normalisation -- and first K/V stages, then the tile's stores, wait for the loads "
+         "only), **ordered** (the stores, then the next unit's loads, one wait "
          "for both: the previous form of this kernel), **coupled** (the stores made visible "
          "device-wide by a device-scope release -- L2 write-back, wait for completion -- before "
          "the next unit's loads: the completion-coupled counterfactual).\n",
