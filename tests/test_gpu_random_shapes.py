@@ -4,7 +4,9 @@ Each case draws B, H, S, D, P, a scale and optionally a block mask from a
 fixed seed, so that the launch plans the ABI picks -- whole rounds, split
 half tiles, the spread last round (lead and helper pieces), half tiles cut
 into key pieces, masked schedules and their plain-order fallback -- meet
-shapes no hand-written case names.  The output must meet the float64 oracle
+shapes no hand-written case names; a second sweep draws longer sequences
+sized so that the _ws_ entry points run the dynamic schedule (the last
+round's tiles in key pieces handed out from a counter).  The output must meet the float64 oracle
 on sampled rows (tile and slab edges, the ragged tail, random rows) -- the
 element-wise bound from the arithmetic in every case, the workload gate in
 the cases at the workloads' scale 1/sqrt(D) -- fill every slab element, and
@@ -94,3 +96,44 @@ def test_random_shape(i):
     assert_within_bound(g, ref, absv, f"case {i}")
     if c["scale"] == 1.0 / math.sqrt(D):
         assert_close(g, ref, f"case {i}")
+
+
+def _dyn_case(i, n):
+    """A seeded shape on which the _ws_ entry points run the dynamic
+    schedule on n CUs: at least one full round of whole 256-query tiles, a
+    last round at least half full, at least 256 key stages per tile."""
+    r = np.random.default_rng(9000 + i)
+    D = int(r.choice([64, 128]))
+    P = int(r.choice([2, 4, 8]))
+    B = int(r.choice([1, 2]))
+    S = P * int(r.integers(16384 // P + 1, 40000 // P + 1))
+    tiles = -(-S // 256)
+    H = next(h for h in range(1, 64)
+             if B * h * tiles >= n + (B * h * tiles) % n and 2 * ((B * h * tiles) % n) >= n)
+    entry = ENTRIES[1 + i % 3]
+    scale = float(r.choice([1.0 / math.sqrt(D), -0.3]))
+    return dict(B=B, H=H, S=S, D=D, P=P, keep=None, scale=scale, entry=entry, seed=9000 + i)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_dynamic_schedule_shape(i):
+    """Seeded shapes that reach the dynamic schedule (last round in key
+    pieces from a counter) through each _ws_ entry point: the float64 oracle
+    on sampled rows, every slab element written, a second call bit-equal."""
+    c = _dyn_case(i, torch.cuda.get_device_properties(0).multi_processor_count)
+    print(f"[dynamic shapes] {i}: {c}", file=sys.stderr, flush=True)
+    B, H, S, D, P = c["B"], c["H"], c["S"], c["D"], c["P"]
+    q, k, v = wl.random_qkv(B, H, S, D, seed=c["seed"])
+    qd, kd, vd = (t.to("cuda:0") for t in (q, k, v))
+    got = _run(c, qd, kd, vd, None)
+    again = _run(c, qd, kd, vd, None)
+    assert torch.equal(got.view(torch.int16), again.view(torch.int16)), "second call differs"
+    rows = sample_rows(S, P, seed=c["seed"], n_random=4)
+    vv = np.concatenate([v.double().numpy(), np.abs(v.double().numpy())], axis=-1)
+    both = oracle.attention(q.double().numpy(), k.double().numpy(), vv, c["scale"], None,
+                            rows=rows)
+    ref, absv = both[..., :D], both[..., D:]
+    g = slab_rows(got, rows, S, P)
+    assert_within_bound(g, ref, absv, f"dynamic case {i}")
+    if c["scale"] == 1.0 / math.sqrt(D):
+        assert_close(g, ref, f"dynamic case {i}")

@@ -111,9 +111,12 @@ def test_slab_inputs_blocking_entry_point():
 
 WS_CASES = {
     # name: (B, H, S, D, P, mask keep probability or None); the last round
-    # spread (lead and helper pieces), cut into half-tile pieces, or masked.
+    # in key pieces from the dynamic schedule's counter, spread (lead and
+    # helper pieces), cut into half-tile pieces, or masked (256 CUs).
     "last round spread, slices on tile bounds": (1, 1, 16384, 128, 2, None),
-    "whole rounds + spread last round": (1, 5, 20000, 128, 4, None),
+    "whole round + spread last round": (1, 4, 20000, 128, 4, None),
+    "dynamic schedule": (1, 5, 20000, 128, 4, None),
+    "dynamic schedule, D = 64, B = 2": (2, 3, 16400, 64, 4, None),
     "half tiles in pieces (Image share)": (1, 3, 4096, 128, 8, None),
     "half tiles in pieces, D = 64, B = 2": (2, 1, 3000, 64, 4, None),
     "block mask, B = 2": (2, 3, 1000, 128, 4, 0.4),
