@@ -62,7 +62,6 @@ constexpr int BN = 64;           // keys per LDS stage
 // Rounds of a masked launch's schedule a workgroup can hold (plain order
 // beyond).
 constexpr int kPlanMaxRounds = 256;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr float kRaise = 256.0f;   // a lane's stage sum that raises the running max
 
 // Tuning knob, overridable at build time (-D): operand reads issued ahead of
@@ -577,8 +576,10 @@ __device__ __forceinline__ uint32_t clock_lo() { return (uint32_t)__builtin_amdg
 // bit for bit.
 //
 // Tile boundary (the piggyback).  When a unit's Q-loop is over, each wave
-// first issues the next unit's prologue -- its Q fragments and the first K/V
-// stages of its stream -- then the finished unit's slab stores, and then
+// first issues the next unit's prologue -- its Q fragments (as soon as the
+// last stage's scores are formed, ahead of the epilogue's merge and
+// normalisation) and the first K/V stages of its stream -- then the
+// finished unit's slab stores, and then
 // waits for the prologue only.  gfx950 counts vector loads and stores on one
 // counter, vmcnt, which retires in issue order: vmcnt(N), N = the vector
 // memory instructions issued after the prologue (the stores), completes every
