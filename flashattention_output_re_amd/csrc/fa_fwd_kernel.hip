@@ -814,25 +814,38 @@ void fa_fwd_pp_kernel(FwdParams p) {
   // that runs past the end of a slab continues in the next slab, (B - 1) Sp
   // rows further on (Sp >= 64, so at most one boundary); keys >= S land
   // past the tensor and read as zeros.
-  auto slab_dma = [&](const Unit& u, uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo,
-                      int key) FA_INL {
-    if (key >= p.S) {
-      dma_blocks<PW>(dst, r, in_bytes, lo);
-      return;
-    }
+  // The stage's address, scalar work that the stage loop does in the MFMA
+  // region before the softmax region that issues the DMA (the softmax wave
+  // is the one whose instruction stream bounds a stage).
+  struct SlabAt {
+    uint32_t base;   // byte offset of the stage's first row
+    int left;        // rows before the slab boundary (>= BN: none in the stage)
+  };
+  auto slab_at = [&](const Unit& u, int key) FA_INL {
+    if (key >= p.S) return SlabAt{in_bytes, BN};
     const uint32_t ps = (__umulhi((uint32_t)key, p.sp_magic) + key) >> p.sp_shift;
-    const uint32_t base = ((ps * p.B + u.b) * p.Sp + (key - ps * p.Sp)) * rowstride + u.head_col;
-    const int left = (int)((ps + 1) * p.Sp) - key;    // rows before the boundary
-    if (left >= BN) {
-      dma_blocks<PW>(dst, r, base, lo);
+    return SlabAt{((ps * p.B + u.b) * p.Sp + (key - ps * p.Sp)) * rowstride + u.head_col,
+                  (int)((ps + 1) * p.Sp) - key};
+  };
+  auto slab_dma_at = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo,
+                         SlabAt a) FA_INL {
+    if (a.left >= BN) {
+      dma_blocks<PW>(dst, r, a.base, lo);
       return;
     }
     const uint32_t delta = (uint32_t)(p.B - 1) * p.Sp * rowstride;
     uint32_t o[PW];
 #pragma unroll
-    for (int q = 0; q < PW; ++q) o[q] = lo[q] + (row0 + q * (64 / Tile<D>::CH) >= left ? delta : 0u);
-    dma_blocks<PW>(dst, r, base, o);
+    for (int q = 0; q < PW; ++q)
+      o[q] = lo[q] + (row0 + q * (64 / Tile<D>::CH) >= a.left ? delta : 0u);
+    dma_blocks<PW>(dst, r, a.base, o);
   };
+  auto slab_dma = [&](const Unit& u, uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo,
+                      int key) FA_INL { slab_dma_at(dst, r, lo, slab_at(u, key)); };
+  // Slab inputs: the addresses of the stages the next softmax region loads
+  // (whole units: K or V stage n + 3, one key for both; split units: K stage
+  // n + 2 and V stage n + 1).
+  SlabAt sl_k{0u, BN}, sl_v{0u, BN};
   // The same share as a DmaPlan ([B][H][S][D] inputs): instruction q reads
   // the byte offsets dma_blocks would use.
   auto plan_of = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t r, const uint32_t* lo, int key) FA_INL {
@@ -921,7 +934,10 @@ void fa_fwd_pp_kernel(FwdParams p) {
   // V stage n + 1 into the slot of V stage n - 1 (read in M(n - 1)).
   auto stage_dma = [&](auto SLOT, int n) FA_INL {
     constexpr int slot = decltype(SLOT)::value;
-    if (SPLIT) {
+    if constexpr (SPLIT && SLAB_IN) {
+      slab_dma_at(kbuf(slot) + 64 * 8 * PW * wq, cur.rk, koff, sl_k);
+      slab_dma_at(vbuf((slot + 1) % NBUF) + 64 * 8 * PW * wq, cur.rv, voff, sl_v);
+    } else if (SPLIT) {
       dma_k(cur, slot, MASKED ? key_n[2] : key_of(cur, n + 2));
       dma_v(cur, (slot + 1) % NBUF, MASKED ? key_n[1] : key_of(cur, n + 1));
     } else if constexpr (!SLAB_IN) {
@@ -931,9 +947,20 @@ void fa_fwd_pp_kernel(FwdParams p) {
       uint16_t* const dst = (grp == 0 ? kbuf(sl) : vbuf(sl)) + 64 * 8 * PW * wq;
       dma_blocks<PW>(dst, grp == 0 ? cur.rk : cur.rv, (uint32_t)key_of(cur, n + 3) * (D * 2), koff);
     } else if (grp == 0) {
-      dma_k(cur, (slot + 3) % NBUF, key_of(cur, n + 3));
+      slab_dma_at(kbuf((slot + 3) % NBUF) + 64 * 8 * PW * wq, cur.rk, koff, sl_k);
     } else {
-      dma_v(cur, (slot + 3) % NBUF, key_of(cur, n + 3));
+      slab_dma_at(vbuf((slot + 3) % NBUF) + 64 * 8 * PW * wq, cur.rv, koff, sl_k);
+    }
+  };
+  // Slab inputs: the addresses for the softmax region of stage n.
+  auto slab_plan = [&](int n) FA_INL {
+    if constexpr (SLAB_IN) {
+      if constexpr (SPLIT) {
+        sl_k = slab_at(cur, MASKED ? key_n[2] : key_of(cur, n + 2));
+        sl_v = slab_at(cur, MASKED ? key_n[1] : key_of(cur, n + 1));
+      } else {
+        sl_k = slab_at(cur, key_of(cur, n + 3));
+      }
     }
   };
   // Split units, [B][H][S][D] inputs: the same stages as DmaPlans, issued
@@ -1056,6 +1083,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
       key_n[1] = key_n[2];
       key_n[2] = kept.next();
     }
+    slab_plan(n + 1);
     barrier_keep_dma();
   };
   // A unit's stages.
@@ -1243,6 +1271,7 @@ void fa_fwd_pp_kernel(FwdParams p) {
     // than 64 keys) weigh exp2(-inf) = 0 rather than NaN.
     m_run = -3.0e38f;
     l_run = 0.0f;
+    slab_plan(0);
 
     stages();
 
