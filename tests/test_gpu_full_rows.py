@@ -1,7 +1,10 @@
 """GPU parity at full size on every row: the fused call through the C ABI
 against the float64 oracle on every output element of the Video-DiT share
 and of the block-sparse Video share (5 heads x 32760 rows each), and on one
-whole head of the long video share (75600 rows).
+whole head of the long video share (75600 rows); then the workspace entry
+point (the headline call, whose last round runs as key pieces from the
+dynamic schedule) on every row of the long share's last head, which holds
+that round's tiles.
 
 Each element meets the workload gate (max-abs <= 1e-2, mean-abs <= 1e-3) and
 the element-wise bound from the arithmetic (gpu_util.assert_within_bound).
@@ -48,3 +51,30 @@ def test_every_row(name, heads):
         assert_within_bound(got, ref, absv, f"{name} head {h}")
         say(f"[full rows] {name} head {h}: {w.S} rows, max_abs {e['max_abs']:.3e} "
             f"mean_abs {e['mean_abs']:.3e} ({time.perf_counter() - t0:.1f} s)")
+
+
+def test_every_row_of_the_long_share_last_head_workspace_form():
+    """The workspace entry point on the long share (the headline call): its
+    last round -- 200 tiles, all of the last head's last 200 query tiles --
+    runs as key pieces handed out from a counter and merged by a second
+    launch; every row of that head against the oracle."""
+    import flashattention_output_re_amd as fa
+    w = wl.WORKLOADS["long"]
+    inp = wl.make("long")
+    h = w.H - 1
+    say(f"[full rows] long, workspace form, head {h}")
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    out = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device=q.device)
+    fa.attn_fwd_relayout_ws_async(q, k, v, out, w.B, w.H, w.S, w.D, w.P, w.scale)
+    torch.cuda.synchronize()
+    got = out.permute(1, 3, 0, 2, 4).reshape(w.B, w.H, w.S, w.D)[:, h:h + 1]
+    got = got.to(torch.float64).cpu().numpy()
+    t0 = time.perf_counter()
+    qd, kd, vd = inp.f64("q"), inp.f64("k"), inp.f64("v")
+    vv = np.concatenate([vd[:, h:h + 1], np.abs(vd[:, h:h + 1])], axis=-1)
+    both = oracle.attention(qd[:, h:h + 1], kd[:, h:h + 1], vv, w.scale, row_block=512)
+    ref, absv = both[..., :w.D], both[..., w.D:]
+    e = assert_close(got, ref, f"long head {h}, workspace form")
+    assert_within_bound(got, ref, absv, f"long head {h}, workspace form")
+    say(f"[full rows] long head {h} (workspace form): {w.S} rows, max_abs {e['max_abs']:.3e} "
+        f"mean_abs {e['mean_abs']:.3e} ({time.perf_counter() - t0:.1f} s)")
