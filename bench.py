@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_output_re_amd/csrc/fa_fwd_kernel.hip",
                   "flashattention_output_re_amd/csrc/fa_fwd_kernel.h"]
 WORKLOAD_KEYS = {"video": "video-dit-share", "long": "long-video-share",
-                 "image": "image-dit-share", "sparse": "block-sparse-video", "tiny": "tiny"}
+                 "image": "image-dit-share", "sparse": "block-sparse-video", "tiny": "tiny",
+                 "video64": "video-dit-share-d64"}
 
 
 # What one fused call launches on its stream (the roofline's "launch" is that
@@ -355,7 +356,8 @@ def write_profile_report(workload: str, d: str):
     min_bytes = 4.0 * w.B * w.H * w.S * w.D * 2
     hsh = kernel_source_hash()
     title = {"video": "Video-DiT share", "long": "long video share", "image": "Image-DiT share",
-             "sparse": "block-sparse video", "tiny": "tiny case"}[workload]
+             "sparse": "block-sparse video", "tiny": "tiny case",
+             "video64": "Video-DiT share at D = 64"}[workload]
     shape = f"B={w.B}, H={w.H}, S={w.S}, D={w.D}, P={w.P}" + (
         f", {100 * float(keep.mean()):.1f}% of 128x128 tiles kept" if keep is not None else "")
 

@@ -51,7 +51,7 @@ def test_workload_full_parity(name):
     say(f"[parity] {name}: {e}")
 
 
-@pytest.mark.parametrize("name", ["video", "long", "sparse"])
+@pytest.mark.parametrize("name", ["video", "long", "sparse", "video64"])
 def test_workload_sampled_parity(name):
     w = wl.WORKLOADS[name]
     say(f"[parity] {name} sampled rows B={w.B} H={w.H} S={w.S} D={w.D} P={w.P}")
@@ -74,7 +74,7 @@ def test_workload_sampled_parity(name):
 
 
 # ------------------------------------------------------ bit-exact re-layout
-@pytest.mark.parametrize("name", ["tiny", "image", "video", "long", "sparse"])
+@pytest.mark.parametrize("name", ["tiny", "image", "video", "long", "sparse", "video64"])
 def test_tags_bit_exact(name):
     w = wl.WORKLOADS[name]
     say(f"[tags] {name} S={w.S} H={w.H} D={w.D} P={w.P}")

@@ -52,7 +52,9 @@ class Workload:
         return self.S // self.P
 
 
-# The five workloads, in a fixed order; the base seed of entry i is 1000 + i.
+# The workloads, in a fixed order; the base seed of entry i is 1000 + i.  The
+# last is the Video share at head dimension 64 (the pages name no head
+# dimension; DiT models use both 64 and 128).
 WORKLOADS = {
     "tiny": Workload("tiny", B=1, H=1, S=256, D=64, P=2, seed=1000),
     "image": Workload("image", B=1, H=3, S=4096, D=128, P=8, seed=1001),
@@ -61,6 +63,8 @@ WORKLOADS = {
     "long": Workload("long", B=1, H=5, S=75600, D=128, P=8, seed=1003),
     "sparse": Workload("sparse", B=1, H=5, S=32760, D=128, P=8, seed=1004,
                        keep_prob=0.3),
+    "video64": Workload("video64", B=1, H=5, S=32760, D=64, P=8, seed=1005,
+                        kscale=(0.5, 2.0)),
 }
 
 DESCRIPTIONS = {
@@ -71,6 +75,8 @@ DESCRIPTIONS = {
     "long": "Long video share: B=1 H=5 S=75600 (21x60x60 latent) D=128 P=8",
     "sparse": "Block-sparse video: B=1 H=5 S=32760 D=128 P=8, 128x128 tiles, "
               "70% sparsity, diagonal kept",
+    "video64": "Video-DiT share at head dimension 64: B=1 H=5 S=32760 D=64 P=8, "
+               "per-head K scale U(0.5,2)",
 }
 
 
