@@ -139,9 +139,10 @@ int relayout_to_slabs_async(const void* plain, void* out_slabs, int B, int H, in
 int relayout_to_slabs(const void* plain, void* out_slabs, int B, int H, int S, int D, int P);
 
 /* The dense calls above run the last, partial round of whole 256-query tiles
- * (when fewer tiles remain than the GPU has resident workgroups) as half
- * tiles inside each workgroup, which needs no memory beyond the caller's
- * tensors.  The _ws_ forms instead share that round among the workgroups.
+ * (when at most half as many tiles remain as the GPU has resident
+ * workgroups; a fuller last round runs as whole tiles) as half tiles, the
+ * keys split between a workgroup's two wave groups, which needs no memory
+ * beyond the caller's tensors.  The _ws_ forms instead share that round among the workgroups.
  * A call of at least one full round whose last round holds t >= G/2 tiles
  * of at least 256 key stages runs a dynamic schedule: the full rounds
  * round-robin, then every later tile -- and the last t tiles cut into P =
