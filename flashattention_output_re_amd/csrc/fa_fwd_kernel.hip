@@ -1471,42 +1471,46 @@ void fa_fwd_pp_kernel(FwdParams p) {
 // online over chunks of up to four partials, each chunk's loads all issued
 // before any is used.  With m the largest running max so far, partial k
 // weighs 2^(m_k - m) l_k, and what is summed is rescaled when m grows.
+// Dim block db (32 dims) of the merge of np partial results for the rows of
+// fused-kernel wave `wave`, each lane standing where that wave's lane stood:
+// with m* the largest running max and weights w = 2^(m - m*) l, acc =
+// sum w O_part and l = sum w, taken online over chunks of kMergeChunk
+// partials, all of a chunk's loads issued before any is used.
+constexpr int kMergeChunk = 8;
 template <int D, class Slot>
 __device__ __forceinline__ void merge_partials(const float* ws, int np, const Slot& slot, int wave,
-                                               int lane, f32x16 (&acc)[D / 32], float& l) {
-  constexpr int NDB = D / 32, NQ = 4 * NDB;
+                                               int db, int lane, f32x16& acc, float& l) {
+  constexpr int NDB = D / 32, NQ = 4 * NDB, C = kMergeChunk;
   typedef float f32x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+  acc = f32x16{};
   l = 0.0f;
   float m = -3.0e38f;
-  for (int k0 = 0; k0 < np; k0 += 4) {
-    f32x4 ml[4], o[4][NQ];
+  for (int k0 = 0; k0 < np; k0 += C) {
+    f32x4 ml[C], o[C][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < C; ++j) {
       // Past np, partial np - 1 again, weighed 0.
       const float* const w = ws + (size_t)slot(k0 + j < np ? k0 + j : np - 1) * seg_floats(D);
       ml[j] = reinterpret_cast<const f32x4*>(w + seg_ml_offset(D))[wave * 64 + lane];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) o[j][q] = reinterpret_cast<const f32x4*>(w)[(wave * NQ + q) * 64 + lane];
+      for (int rr = 0; rr < 4; ++rr)
+        o[j][rr] = reinterpret_cast<const f32x4*>(w)[(wave * NQ + db * 4 + rr) * 64 + lane];
     }
     float mc = m;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < C; ++j)
       if (k0 + j < np) mc = fmaxf(mc, ml[j][0]);
     const float sc = __builtin_amdgcn_exp2f(m - mc);
     l *= sc;
+    acc *= sc;
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) acc[i] *= sc;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < C; ++j) {
       const float a = k0 + j < np ? __builtin_amdgcn_exp2f(ml[j][0] - mc) * ml[j][1] : 0.0f;
       l += a;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q)
+      for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[q / 4][4 * (q % 4) + c] = __builtin_fmaf(a, o[j][q][c], acc[q / 4][4 * (q % 4) + c]);
+        for (int c = 0; c < 4; ++c) acc[4 * rr + c] = __builtin_fmaf(a, o[j][rr][c], acc[4 * rr + c]);
     }
     m = mc;
   }
@@ -1524,7 +1528,6 @@ __device__ __forceinline__ void merge_partials(const float* ws, int np, const Sl
 // and the tile is rounded and stored like a whole unit's (merge_partials).
 template <int D, StoreMode MODE>
 __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
-  constexpr int NDB = D / 32;
   const int lane = threadIdx.x;
   const int wave = blockIdx.y;
   const int l32 = lane & 31, g = lane >> 5;
@@ -1542,12 +1545,13 @@ __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
   auto slot = [&](int k) {
     return dyn ? ti * p.dyn_pieces + k : k == 0 ? ti : p.tail + ti + h0 + k - 1;
   };
-  f32x16 acc[NDB];
+  const int db = blockIdx.z;
+  f32x16 acc[1];
   float l;
-  merge_partials<D>(p.ws, np, slot, wave, lane, acc, l);
+  merge_partials<D>(p.ws, np, slot, wave, db, lane, acc[0], l);
   // l is already the whole row's (each partial's sum covers both wave halves).
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  store_rows<D, MODE, NDB>(p, acc, inv, qt * 256 + wave * 32 + l32, 0, b, h, bh, g, lane);
+  store_rows<D, MODE, 1>(p, acc, inv, qt * 256 + wave * 32 + l32, 32 * db, b, h, bh, g, lane);
 }
 
 // Merge of a split launch cut into pieces: one workgroup of one wave per half
@@ -1557,7 +1561,6 @@ __global__ __launch_bounds__(64) void fa_merge_kernel(FwdParams p) {
 // unit's.
 template <int D, StoreMode MODE>
 __global__ __launch_bounds__(64) void fa_merge_split_kernel(FwdParams p) {
-  constexpr int NDB = D / 32;
   const int lane = threadIdx.x;
   const int wave = blockIdx.y;
   const int l32 = lane & 31, g = lane >> 5;
@@ -1567,12 +1570,13 @@ __global__ __launch_bounds__(64) void fa_merge_split_kernel(FwdParams p) {
   const int b = bh / p.H, h = bh - b * p.H;
   const int np = p.split_pieces;
   auto slot = [&](int k) { return hf * np + k; };
-  f32x16 acc[NDB];
+  const int db = blockIdx.z;
+  f32x16 acc[1];
   float l;
-  merge_partials<D>(p.ws, np, slot, wave, lane, acc, l);
+  merge_partials<D>(p.ws, np, slot, wave, db, lane, acc[0], l);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  store_rows<D, MODE, NDB>(p, acc, inv, qt * 256 + (hf & 1) * 128 + wave * 32 + l32, 0, b, h, bh,
-                           g, lane);
+  store_rows<D, MODE, 1>(p, acc, inv, qt * 256 + (hf & 1) * 128 + wave * 32 + l32, 32 * db, b, h,
+                         bh, g, lane);
 }
 
 __global__ void fa_queue_reset_kernel(int* queue) { *queue = 0; }
@@ -1663,13 +1667,13 @@ static int launch_instr(int instr, const FwdParams& p, int grid_cap, hipStream_t
 
 template <int D, StoreMode MODE>
 static int launch_merge_dm(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_merge_kernel<D, MODE>), dim3(p.tail, 8), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((fa_merge_kernel<D, MODE>), dim3(p.tail, 8, D / 32), dim3(64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <int D, StoreMode MODE>
 static int launch_merge_split_dm(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_merge_split_kernel<D, MODE>), dim3(p.units / p.split_pieces, 4),
+  hipLaunchKernelGGL((fa_merge_split_kernel<D, MODE>), dim3(p.units / p.split_pieces, 4, D / 32),
                      dim3(64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
