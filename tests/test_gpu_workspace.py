@@ -232,3 +232,31 @@ def test_ws_graph_capture_replays(shape):
         torch.cuda.synchronize()
         assert torch.isfinite(busy)
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+
+
+def test_ws_shared_between_shapes_and_plans():
+    """One workspace serves calls of different shapes and launch plans in
+    turn -- the dynamic schedule (its counter after the partial slots), the
+    spread last round and split half tiles in pieces -- and each call equals
+    the same call on a fresh workspace bit for bit: nothing a call leaves in
+    the workspace reaches the next."""
+    shapes = [(1, 5, 20000, 128, 4), (1, 1, 16384, 128, 2), (1, 3, 4096, 128, 8),
+              (2, 3, 16400, 64, 4)]
+    need = max(binding.attn_fwd_workspace_bytes(B, H, S, D) for B, H, S, D, _ in shapes)
+    shared = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    cases = []
+    for i, (B, H, S, D, P) in enumerate(shapes):
+        q, k, v = (to_dev(t) for t in wl.random_qkv(B, H, S, D, seed=300 + i))
+        fresh = torch.empty(binding.attn_fwd_workspace_bytes(B, H, S, D), dtype=torch.uint8,
+                            device="cuda:0")
+        ref = torch.empty((P, B, S // P, H, D), dtype=torch.bfloat16, device="cuda:0")
+        fa.attn_fwd_relayout_ws_async(q, k, v, ref, B, H, S, D, P, 0.1, None, fresh)
+        cases.append((q, k, v, ref, (B, H, S, D, P)))
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        for q, k, v, ref, (B, H, S, D, P) in cases:
+            out = torch.full_like(ref, float("nan"))
+            fa.attn_fwd_relayout_ws_async(q, k, v, out, B, H, S, D, P, 0.1, None, shared)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), \
+                f"round {rnd}, shape {(B, H, S, D, P)}"
