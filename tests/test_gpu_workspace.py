@@ -260,3 +260,29 @@ def test_ws_shared_between_shapes_and_plans():
             torch.cuda.synchronize()
             assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), \
                 f"round {rnd}, shape {(B, H, S, D, P)}"
+
+
+def test_ws_concurrent_calls_on_two_streams():
+    """Two dynamic-schedule calls in flight at once on two streams, each with
+    its own workspace (its own counter), give the results of the same calls
+    made one at a time."""
+    B, H, S, D, P = 1, 5, 20000, 128, 4
+    ins = [tuple(to_dev(t) for t in wl.random_qkv(B, H, S, D, seed=400 + i)) for i in range(2)]
+    need = binding.attn_fwd_workspace_bytes(B, H, S, D)
+    wss = [torch.empty(need, dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    refs = []
+    for (q, k, v), ws in zip(ins, wss):
+        r = torch.empty((P, B, S // P, H, D), dtype=torch.bfloat16, device="cuda:0")
+        fa.attn_fwd_relayout_ws_async(q, k, v, r, B, H, S, D, P, 0.1, None, ws)
+        refs.append(r)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [torch.full_like(refs[0], float("nan")) for _ in range(2)]
+    for rep in range(3):
+        for (q, k, v), ws, o, st in zip(ins, wss, outs, streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                fa.attn_fwd_relayout_ws_async(q, k, v, o, B, H, S, D, P, 0.1, None, ws)
+        torch.cuda.synchronize()
+        for o, r in zip(outs, refs):
+            assert torch.equal(o.view(torch.int16), r.view(torch.int16)), f"repeat {rep}"
