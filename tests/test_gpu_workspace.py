@@ -8,8 +8,10 @@ D = 64 with B = 2, a ragged sequence -- is compared with the float64 oracle
 (every row of one head, sampled rows otherwise) under the gate and the
 element-wise bound, and with integer tags bit for bit inside canary guard
 bands.  Every row of the Video share's all-tail head is compared too.  The
-plain twin equals the slab form bit for bit; repeated calls and HIP-graph
-replays are bit-identical; a workspace that is too small or misaligned is
+plain twin equals the slab form bit for bit; repeated calls, HIP-graph
+replays, calls of different shapes and plans sharing one workspace, and two
+calls in flight on two streams with their own workspaces are bit-identical
+to the calls made alone; a workspace that is too small or misaligned is
 rejected before any launch.
 """
 import math
